@@ -1,0 +1,363 @@
+#!/usr/bin/env python3
+"""Throughput of the W8A8 INT8 projection path on one MI355X.
+
+A step is one pass of the whole hot path over the workload's synthetic
+input, all of it in the library's HIP kernels on one stream:
+  per block: quantize X (shared by Q, K, V) -> 3 GEMMs; quantize X -> O GEMM;
+  quantize X -> FC1 GEMM; SiLU+quantize of FC1's output -> FC2 GEMM;
+  between blocks (the sweep): power-of-two renormalization of FC2's output
+  feeds the next block.
+Inputs and weights are resident in HBM before timing starts.  Reported:
+  value      = sum of 2*M*N*K over the step's GEMMs / step time (TOPS),
+               quantization and glue time included;
+  roofline   = the INT8 GEMM kernel alone: its algorithmic ops / its
+               average launch time (HIP events around every launch), against
+               the dense INT8 MFMA peak of 5.0 POP/s;
+  cpu_baseline = the CPU oracle timed on a bounded row sample;
+  bf16_baseline (context) = torch's BF16 linear (hipBLASLt) on the same
+               shapes.
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 0-4]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+INT8_PEAK_TOPS = 5000.0   # MI355X dense INT8 MFMA, published
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 MFMA, published
+METRIC = ("W8A8 projection TOPS and % INT8 MFMA peak at DiT shapes "
+          "(M~19k, K=5376)")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", type=int, default=4, choices=range(5))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--check-rows", type=int, default=2)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def projections_of(wl, D):
+    return list(wl.projs)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the projection shards by tokens with no exchange; see the "
+              "design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import __graft_entry__
+    __graft_entry__._ensure_built()
+    from w8a8_int8_gemm_amd import binding as B
+    from w8a8_int8_gemm_amd import block as BL
+    from w8a8_int8_gemm_amd import datagen as D
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    wl = D.WORKLOADS[args.config]
+    M = wl.M
+    single = len(wl.projs) == 1
+    threads = min(16, os.cpu_count() or 8)
+
+    # ---- oracle sample (row chain), computed while weights are on the host
+    orc = None
+    rows = None
+    if not args.no_check or not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.default()
+    x0_host = D.activations(M, D.HIDDEN, wl.seed)
+    if not args.no_check:
+        rows = D.row_sample(M, max(args.check_rows - 2, 0), wl.seed)
+        chk_x = x0_host[rows]
+        chk_out = None
+
+    # ---- weights: generated per block on the host, resident on the GPU
+    t0 = time.time()
+    blocks = []
+    for b in range(wl.blocks):
+        params = D.block_params(wl, b, threads=threads)
+        blocks.append({p.name: BL.upload_proj(p, params[p.name], dev)
+                       for p in wl.projs})
+        if rows is not None:
+            if single:
+                p = wl.projs[0]
+                pp = params[p.name]
+                chk_out = {p.name: orc.linear(chk_x, pp.w, pp.sw, pp.bias)}
+            else:
+                chk_out = {}
+                for n in ("q", "k", "v", "o", "fc1"):
+                    pp = params[n]
+                    chk_out[n] = orc.linear(chk_x, pp.w, pp.sw, pp.bias)
+                h = orc.silu_bf16(chk_out["fc1"])
+                pp = params["fc2"]
+                chk_out["fc2"] = orc.linear(h, pp.w, pp.sw, pp.bias)
+                if b + 1 < wl.blocks:
+                    chk_x = orc.pow2_renorm(chk_out["fc2"])
+        del params
+    torch.cuda.synchronize()
+    log(f"[bench] {wl.name}: M={M}, {wl.blocks} block(s), weights resident "
+        f"({sum(p.w.numel() for blk in blocks for p in blk.values())/1e9:.2f}"
+        f" GB INT8) in {time.time() - t0:.1f}s")
+
+    x0 = BL.to_device_bf16(x0_host, dev)
+    xbuf = [torch.empty_like(x0), torch.empty_like(x0)]
+    runner = BL.BlockRunner(M, dev) if not single else None
+    if single:
+        p0 = wl.projs[0]
+        qbuf = torch.empty((M, p0.K), dtype=torch.int8, device=dev)
+        sbuf = torch.empty((M,), dtype=torch.float32, device=dev)
+        ybuf = torch.empty((M, p0.N), dtype=torch.bfloat16, device=dev)
+        wsb = torch.empty((max(B.workspace_bytes(M, p0.N, p0.K), 256),),
+                          dtype=torch.uint8, device=dev)
+
+    ops_per_step = 0
+    for blk in blocks:
+        for p in blk.values():
+            ops_per_step += 2 * M * p.N * p.K
+
+    gemm_events = []
+
+    def on_gemm(name, phase):
+        if gemm_events is None:
+            return
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record()
+        gemm_events.append(ev)
+
+    def step(record):
+        nonlocal gemm_events
+        gemm_events = [] if record else None
+        if single:
+            p = blocks[0][wl.projs[0].name]
+            B.quantize_act(x0, out=(qbuf, sbuf))
+            on_gemm(p.name, "begin")
+            B.gemm(qbuf, sbuf, p.w, p.sw, p.bias, out=ybuf, workspace=wsb)
+            on_gemm(p.name, "end")
+            return {p.name: ybuf}
+        x = x0
+        out = None
+        for b, blk in enumerate(blocks):
+            out = runner.run(x, blk, on_gemm=on_gemm)
+            if b + 1 < len(blocks):
+                nxt = xbuf[b % 2]
+                B.pow2_renorm(out["fc2"], out=nxt)
+                x = nxt
+        return out
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    all_gemm = []
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        out = step(True)
+        all_gemm.append(gemm_events)
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / max(args.steps, 1)
+    tops = ops_per_step / (ms_per_step * 1e-3) / 1e12
+
+    # per-launch GEMM durations
+    gemm_ms = 0.0
+    launches = 0
+    for evs in all_gemm:
+        for i in range(0, len(evs), 2):
+            gemm_ms += evs[i].elapsed_time(evs[i + 1])
+            launches += 1
+    gemm_ops = ops_per_step * args.steps
+    gemm_tops = gemm_ops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None
+    avg_launch_us = gemm_ms * 1e3 / max(launches, 1)
+    log(f"[bench] step {ms_per_step:.3f} ms -> {tops:.1f} TOPS "
+        f"({100 * tops / INT8_PEAK_TOPS:.1f}% of INT8 peak); GEMM kernel "
+        f"{gemm_tops:.1f} TOPS, avg launch {avg_launch_us:.1f} us")
+
+    # ---- sampled-row oracle check of the last step (outside timing)
+    check = None
+    if rows is not None:
+        ri = torch.from_numpy(rows).to(dev)
+        ok = True
+        for n, ref in chk_out.items():
+            got = BL.from_device_bf16(out[n][ri])
+            ok &= bool(np.array_equal(got, ref))
+        check = {"rows": rows.tolist(), "bit_exact": ok}
+        log(f"[bench] oracle check of rows {rows.tolist()} through "
+            f"{wl.blocks} block(s): {'bit-exact' if ok else 'MISMATCH'}")
+
+    # ---- BF16 baseline (hipBLASLt through torch), same shapes, one block
+    bf16 = None
+    if not args.no_bf16_baseline:
+        bf16 = bf16_baseline(torch, D, BL, wl, x0, blocks[0], dev,
+                             args.warmup, max(args.steps, 3))
+        log(f"[bench] BF16 baseline: {bf16['tflops']:.1f} TFLOPS")
+
+    # ---- CPU baseline: the oracle on a bounded row sample
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(orc, D, wl, x0_host, args.cpu_seconds, threads)
+        log(f"[bench] CPU oracle: {cpu['value']:.4f} TOPS on {cpu['cores']} "
+            f"threads ({cpu['sample']})")
+
+    gemm_shapes = sorted({(M, p.N, p.K) for p in blocks[0].values()})
+    result = {
+        "metric": METRIC,
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "tokens": M,
+            "blocks": wl.blocks,
+            "linears": wl.blocks * len(wl.projs),
+            "gemm_shapes_MNK": [list(s) for s in gemm_shapes],
+            "parallelism": "single_gpu",
+        },
+        "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
+        "roofline": {
+            "kernel": "gemm_kernel (INT8 MFMA + fused epilogue)",
+            "bound": "mfma",
+            "achieved": round(gemm_tops, 2) if gemm_tops else None,
+            "peak": INT8_PEAK_TOPS,
+            "unit": "TOP/s",
+            "frac": round(gemm_tops / INT8_PEAK_TOPS, 4) if gemm_tops else None,
+            "avg_launch_us": round(avg_launch_us, 2),
+            "launches_timed": launches,
+            "traffic": traffic_entry(),
+        },
+        "cpu_baseline": cpu,
+        "bf16_baseline": bf16,
+        "oracle_check": check,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def traffic_entry():
+    """Measured HBM bytes per GEMM launch from committed rocprofv3 counter
+    summaries, valid only while the kernel source is unchanged."""
+    import hashlib
+    f = ROOT / "profiles" / "gemm_traffic.json"
+    src = ROOT / "w8a8_int8_gemm_amd" / "csrc" / "gemm.hip"
+    if not f.exists():
+        return None
+    rec = json.loads(f.read_text())
+    sha = hashlib.sha256(src.read_bytes()).hexdigest()
+    if rec.get("kernel_sha256") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def bf16_baseline(torch, D, BL, wl, x0, blk, dev, warmup, reps):
+    """torch.nn.functional.linear in BF16 (hipBLASLt) on the same shapes:
+    weights are the dequantized INT8 weights rounded to BF16."""
+    F = torch.nn.functional
+    ws = {n: (p.w.to(torch.float32) * p.sw[:, None]).to(torch.bfloat16)
+          for n, p in blk.items()}
+    bs = {n: p.bias for n, p in blk.items()}
+    ops = sum(2 * x0.shape[0] * p.N * p.K for p in blk.values())
+
+    def run():
+        if len(blk) == 1:
+            n = next(iter(blk))
+            return F.linear(x0, ws[n], bs[n])
+        for n in ("q", "k", "v", "o"):
+            F.linear(x0, ws[n], bs[n])
+        h = F.linear(x0, ws["fc1"], bs["fc1"])
+        return F.linear(F.silu(h), ws["fc2"], bs["fc2"])
+
+    for _ in range(warmup + 1):
+        run()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        run()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    tflops = ops / (ms * 1e-3) / 1e12
+    del ws
+    return {"tflops": round(tflops, 2), "ms_per_block": round(ms, 4),
+            "pct_bf16_peak": round(100 * tflops / BF16_PEAK_TFLOPS, 2),
+            "what": "torch.nn.functional.linear, BF16 weights, one block "
+                    "(SiLU included)"}
+
+
+def cpu_baseline(orc, D, wl, x0_host, seconds, threads):
+    """The oracle as it stands, timed on the first rows of block 0's
+    projections; rows are doubled until the run lasts `seconds`/4, then one
+    final timed run with about `seconds` of work."""
+    params = D.block_params(wl, 0, threads=threads)
+    K = D.HIDDEN
+
+    def run(R):
+        x = x0_host[:R]
+        macs = 0
+        t = time.perf_counter()
+        if len(wl.projs) == 1:
+            p = wl.projs[0]
+            pp = params[p.name]
+            orc.linear(x, pp.w, pp.sw, pp.bias)
+            macs += R * p.N * p.K
+        else:
+            for n in ("q", "k", "v", "o", "fc1"):
+                pp = params[n]
+                y = orc.linear(x, pp.w, pp.sw, pp.bias)
+                macs += R * pp.w.shape[0] * K
+            h = orc.silu_bf16(y)
+            pp = params["fc2"]
+            orc.linear(h, pp.w, pp.sw, pp.bias)
+            macs += R * pp.w.shape[0] * pp.w.shape[1]
+        return time.perf_counter() - t, macs
+
+    R = 4
+    dt, _ = run(R)
+    while dt < seconds / 4 and R < wl.M:
+        R = min(R * 2, wl.M)
+        dt, _ = run(R)
+    R = int(min(wl.M, max(1, R * seconds / max(dt, 1e-3))))
+    dt, macs = run(R)
+    return {"value": round(2 * macs / dt / 1e12, 6), "unit": "TOPS",
+            "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"first {R} of {wl.M} token rows through block 0's "
+                      f"{len(wl.projs)} projection(s), {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,178 @@
+/*
+ * w8a8.h -- C ABI of the MI355X (gfx950) W8A8 INT8 projection library.
+ *
+ * The operation is the INT8 projection GEMM inside each block of a
+ * MiniMax-H3-style audio/video diffusion transformer: Q, K, V, attention
+ * output, FC1 and FC2 run with INT8 weights and per-token INT8 activations
+ * at the model's native hidden width (5376), without padding K and without
+ * dequantizing the weights ("feat(mps): support MiniMax-H3 INT8 inference
+ * on Apple M5", LightX2V pull request #1672: description, commit notes and
+ * "Changes" table).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensors are dense and row-major, with no leading-dimension
+ *     arguments.  BF16 values are passed as their 16-bit patterns.
+ *   - Device pointers only (memory the caller allocated on the current HIP
+ *     device); the caller owns every buffer, including any workspace.  The
+ *     library never allocates, frees or synchronizes.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *     kernels on it and return without waiting.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     error nothing is launched and no output is touched.  A launch failure
+ *     returns W8A8_ERR_HIP; a device fault surfaces at the caller's next
+ *     synchronization.
+ *   - The current device must be a gfx950 GPU; otherwise W8A8_ERR_DEVICE
+ *     (there is no other code path).
+ *   - Calls on one stream are ordered; concurrent calls on different
+ *     streams are safe as long as their output buffers do not overlap.
+ *   - Not checked on the device (documented preconditions): activations are
+ *     finite; weight scales are finite and > 0 (the converter on the
+ *     LightX2V page validates exactly this, "Validation").
+ */
+#ifndef W8A8_H
+#define W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W8A8_OUT_BF16 = 0, /* y: uint16 BF16 bits [M,N]                        */
+  W8A8_OUT_FP32 = 1, /* y: float [M,N], the epilogue before BF16 rounding */
+  W8A8_OUT_I32 = 2   /* y: int32 [M,N], the raw INT32 accumulators        */
+} w8a8_out_t;
+
+typedef enum {
+  W8A8_OK = 0,
+  W8A8_ERR_NULL = 1,      /* a required pointer is NULL                  */
+  W8A8_ERR_SHAPE = 2,     /* a size violates the shape contract          */
+  W8A8_ERR_ALIGN = 3,     /* a pointer is not aligned as required        */
+  W8A8_ERR_WORKSPACE = 4, /* workspace missing or smaller than required  */
+  W8A8_ERR_OUT_DTYPE = 5, /* unknown output type                         */
+  W8A8_ERR_ALIAS = 6,     /* an output overlaps an input or other output */
+  W8A8_ERR_DEVICE = 7,    /* no HIP device, or it is not gfx950          */
+  W8A8_ERR_HIP = 8        /* a HIP call or kernel launch failed          */
+} w8a8_status_t;
+
+/* Largest K accepted by w8a8_gemm / w8a8_linear: with INT8 operands every
+ * product is at most 128*128 = 2^14 in magnitude, so the INT32 accumulator
+ * cannot overflow while K*2^14 <= 2^31 - 1; 130944 is the largest multiple
+ * of 128 below that bound. */
+#define W8A8_MAX_K 130944
+
+/*
+ * Per-token activation quantization.
+ *   x        BF16 [M,K], 16-byte aligned.
+ *   a_q      INT8 [M,K] out, 8-byte aligned.
+ *   a_scale  FP32 [M] out, 4-byte aligned.
+ * For each row m: amax = max_k |x[m,k]|; a_scale[m] = amax / 127 (binary32
+ * division, round to nearest even); a_q[m,k] = x[m,k] / a_scale[m] divided
+ * in binary32 and rounded to the nearest integer, ties to even, clamped to
+ * [-127, 127].  A row of zeros gives a_scale = 0 and zero codes.  FP32
+ * subnormals are kept.
+ * Shape: 1 <= M < 2^31, 8 <= K <= 90112 and K % 8 == 0 (16-byte rows of
+ * BF16; a row stays in registers, 44 chunks per lane); rows whose
+ * length is not a multiple of the kernel's chunk width are handled by
+ * masking the partial chunk, as the LightX2V page's quantizer does
+ * (commit notes, "Changes" table).
+ * Errors: NULL, SHAPE, ALIGN, ALIAS (a_q or a_scale overlapping x or each
+ * other), DEVICE, HIP.
+ */
+int w8a8_quantize_act(const uint16_t *x, int64_t M, int64_t K, int8_t *a_q,
+                      float *a_scale, void *stream);
+
+/*
+ * INT8 GEMM with fused dequantization epilogue.
+ *   a_q       INT8 [M,K] activation codes, 16-byte aligned.
+ *   a_scale   FP32 [M] per-token scales, 4-byte aligned.
+ *   w_q       INT8 [N,K] weights in a Linear's stored layout (one row per
+ *             output channel), 16-byte aligned, consumed as stored.
+ *   w_scale   FP32 [N] per-output-channel scales (finite, > 0), 16-byte
+ *             aligned.
+ *   bias      BF16 [N] or NULL (no bias), 8-byte aligned.
+ *   out       [M,N] of the type selected by out_dtype, 16-byte aligned.
+ *   out_dtype W8A8_OUT_BF16, W8A8_OUT_FP32 or W8A8_OUT_I32.
+ *   workspace device scratch of at least w8a8_workspace_bytes(M, N, K)
+ *             bytes (may be NULL when that is 0), 256-byte aligned.
+ * acc[m,n] = sum_k a_q[m,k] * w_q[n,k] exactly in INT32;
+ * t = ((float)acc * a_scale[m]) * w_scale[n] + bf16->f32(bias[n]), each
+ * operation rounded in binary32 with no fused multiply-add; BF16 output is
+ * t rounded once to nearest even.  Adding the bias before the one rounding
+ * follows "MLX implementation and experiment report" (MiniMax-H3-Image-mlx),
+ * "What the default preserves".
+ * Shape: 1 <= M < 2^31; N and K positive multiples of 128 (the LightX2V
+ * page's shape contract, commit notes); N < 2^31; K <= W8A8_MAX_K.
+ * Errors: NULL, SHAPE, ALIGN, WORKSPACE, OUT_DTYPE, ALIAS, DEVICE, HIP.
+ */
+int w8a8_gemm(const int8_t *a_q, const float *a_scale, const int8_t *w_q,
+              const float *w_scale, const uint16_t *bias, void *out,
+              int out_dtype, int64_t M, int64_t N, int64_t K,
+              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Whole projection: w8a8_quantize_act of x into the workspace, then
+ * w8a8_gemm with BF16 output.  y = bf16(((float)acc*sa[m])*sw[n] + bias[n]).
+ *   x   BF16 [M,K] (16-byte aligned); y BF16 [M,N] (16-byte aligned);
+ *   the other arguments as for w8a8_gemm.
+ * Workspace: at least w8a8_linear_workspace_bytes(M, N, K) bytes, 256-byte
+ * aligned, not overlapping any argument.  K <= 90112 (the quantizer's bound).
+ * Errors: as w8a8_gemm.
+ */
+int w8a8_linear(const uint16_t *x, const int8_t *w_q, const float *w_scale,
+                const uint16_t *bias, uint16_t *y, int64_t M, int64_t N,
+                int64_t K, void *workspace, size_t workspace_bytes,
+                void *stream);
+
+/* Workspace bytes w8a8_gemm needs for this shape (0 when none); 0 as well
+ * for shapes the contract rejects. */
+size_t w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* Workspace bytes w8a8_linear needs: quantized activations, their scales
+ * and w8a8_gemm's own workspace, each 256-byte aligned. */
+size_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* Static description of a status code (never NULL). */
+const char *w8a8_status_string(int status);
+
+/* hipError_t code of the last W8A8_ERR_HIP returned on this thread (0 if
+ * none yet), for diagnostics. */
+int w8a8_last_hip_error(void);
+
+/*
+ * Glue between projections (not part of the W8A8 method; it produces the
+ * inputs a DiT block feeds to FC2 and to the next block).
+ *
+ * w8a8_silu_bf16: y[i] = x / (1 + exp(-x)) correctly rounded to BF16
+ *   (evaluated in FP32, with FP64 for the rare elements whose FP32 value
+ *   lies too close to a BF16 rounding midpoint to decide), for n elements; x and y 16-byte aligned, n >= 0 and n % 8 == 0; x and y
+ *   may be the same buffer (in place) but must not partially overlap.
+ *   Between FC1 and FC2 the block applies SiLU to the BF16 output of FC1
+ *   ("MLX implementation and experiment report", "What the default
+ *   preserves": SiLU rounding follows the original recipe).
+ *
+ * w8a8_pow2_renorm: each row of x [M,K] is multiplied by 2^-e, where
+ *   e = floor(log2(max_k |x[m,k]|)), and rounded to BF16 (all-zero rows
+ *   are copied).  Per-token symmetric quantization is exactly invariant to
+ *   such a scaling, so chaining blocks through it changes no INT8 code
+ *   while keeping BF16 activations finite.  K % 8 == 0, 16-byte aligned;
+ *   in place allowed.
+ *
+ * w8a8_quantize_act_silu: w8a8_silu_bf16 followed by w8a8_quantize_act in
+ *   one pass over x (the SiLU values are rounded to BF16 before they are
+ *   quantized, exactly as the two separate calls do); the BF16 SiLU output
+ *   is not written.  Arguments and errors as w8a8_quantize_act.
+ */
+int w8a8_silu_bf16(const uint16_t *x, uint16_t *y, int64_t n, void *stream);
+int w8a8_pow2_renorm(const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
+                     void *stream);
+int w8a8_quantize_act_silu(const uint16_t *x, int64_t M, int64_t K,
+                           int8_t *a_q, float *a_scale, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8_H */

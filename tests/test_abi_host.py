@@ -1,0 +1,172 @@
+"""The C-ABI library on the host: it loads, exports every symbol that
+include/w8a8.h declares, and rejects bad arguments before launching
+anything.  No kernel is launched here: every call below fails validation,
+which happens before the library touches the device.  Pointers are fake
+addresses that are never dereferenced."""
+from __future__ import annotations
+
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from w8a8_int8_gemm_amd import binding as B
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "w8a8.h"
+
+OK, NULL, SHAPE, ALIGN, WORKSPACE, OUT_DTYPE, ALIAS, DEVICE, HIP = range(9)
+
+# Fake, well-separated, 4 KiB-aligned device addresses.
+A = 0x10_0000_0000
+BUF = {name: A + i * 0x1_0000_0000 for i, name in enumerate(
+    ["x", "aq", "sa", "w", "sw", "bias", "out", "ws"])}
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w8a8_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_api():
+    names = declared_functions()
+    for n in ["w8a8_quantize_act", "w8a8_gemm", "w8a8_linear",
+              "w8a8_workspace_bytes", "w8a8_status_string"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(str(B.LIB_PATH))
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+    # and the binding wraps exactly the declared set
+    assert sorted(B.SIGNATURES) == declared_functions()
+
+
+def test_status_strings():
+    lib = B.lib()
+    seen = set()
+    for code in range(9):
+        s = lib.w8a8_status_string(code)
+        assert s and s not in seen
+        seen.add(s)
+    assert lib.w8a8_status_string(99) == b"unknown status"
+
+
+def gemm(**kw):
+    a = dict(aq=BUF["aq"], sa=BUF["sa"], w=BUF["w"], sw=BUF["sw"],
+             bias=BUF["bias"], out=BUF["out"], dt=0, M=64, N=256, K=256,
+             ws=BUF["ws"], wsb=1 << 30)
+    a.update(kw)
+    return B.lib().w8a8_gemm(a["aq"], a["sa"], a["w"], a["sw"], a["bias"],
+                             a["out"], a["dt"], a["M"], a["N"], a["K"],
+                             a["ws"], a["wsb"], None)
+
+
+def quant(**kw):
+    a = dict(x=BUF["x"], M=4, K=5376, q=BUF["aq"], s=BUF["sa"])
+    a.update(kw)
+    return B.lib().w8a8_quantize_act(a["x"], a["M"], a["K"], a["q"], a["s"],
+                                     None)
+
+
+def linear(**kw):
+    a = dict(x=BUF["x"], w=BUF["w"], sw=BUF["sw"], bias=BUF["bias"],
+             y=BUF["out"], M=64, N=256, K=256, ws=BUF["ws"], wsb=1 << 30)
+    a.update(kw)
+    return B.lib().w8a8_linear(a["x"], a["w"], a["sw"], a["bias"], a["y"],
+                               a["M"], a["N"], a["K"], a["ws"], a["wsb"],
+                               None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(aq=None), NULL), (dict(sa=None), NULL), (dict(w=None), NULL),
+    (dict(sw=None), NULL), (dict(out=None), NULL),
+    (dict(M=0), SHAPE), (dict(M=-5), SHAPE), (dict(N=0), SHAPE),
+    (dict(N=100), SHAPE), (dict(N=5376 + 64), SHAPE), (dict(K=5376 + 8), SHAPE),
+    (dict(K=0), SHAPE), (dict(K=B.MAX_K + 128), SHAPE), (dict(M=1 << 31), SHAPE),
+    (dict(dt=3), OUT_DTYPE), (dict(dt=-1), OUT_DTYPE),
+    (dict(aq=BUF["aq"] + 8), ALIGN), (dict(w=BUF["w"] + 4), ALIGN),
+    (dict(out=BUF["out"] + 2), ALIGN), (dict(sw=BUF["sw"] + 4), ALIGN),
+    (dict(sa=BUF["sa"] + 2), ALIGN), (dict(bias=BUF["bias"] + 2), ALIGN),
+    (dict(out=BUF["aq"]), ALIAS), (dict(out=BUF["w"] + 1024), ALIAS),
+    (dict(out=BUF["sw"] - 16), ALIAS), (dict(out=BUF["bias"]), ALIAS),
+])
+def test_gemm_rejects(kw, code):
+    assert gemm(**kw) == code
+
+
+def test_gemm_workspace_checks():
+    # M = 64 plans split-K and needs a workspace
+    need = B.workspace_bytes(64, 5376, 5376)
+    assert need > 0
+    assert gemm(M=64, N=5376, K=5376, ws=None, wsb=0) == WORKSPACE
+    assert gemm(M=64, N=5376, K=5376, wsb=need - 1) == WORKSPACE
+    assert gemm(M=64, N=5376, K=5376, ws=BUF["ws"] + 16, wsb=need) == ALIGN
+    assert gemm(M=64, N=5376, K=5376, ws=BUF["out"], wsb=need) == ALIAS
+
+
+def test_workspace_sizes():
+    # large M needs none; skinny M needs INT32 partials per split
+    assert B.workspace_bytes(19077, 5376, 5376) == 0
+    assert B.workspace_bytes(37503, 5376, 21504) == 0
+    ws = B.workspace_bytes(64, 5376, 5376)
+    assert ws % (64 * 5376 * 4) == 0 and ws // (64 * 5376 * 4) >= 2
+    assert B.workspace_bytes(64, 100, 5376) == 0  # rejected shape
+    lw = B.linear_workspace_bytes(19077, 5376, 5376)
+    assert lw >= 19077 * 5376 + 19077 * 4 and lw % 256 == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), NULL), (dict(q=None), NULL), (dict(s=None), NULL),
+    (dict(M=0), SHAPE), (dict(K=4), SHAPE), (dict(K=5377), SHAPE),
+    (dict(K=B.QUANT_MAX_K + 8), SHAPE),
+    (dict(x=BUF["x"] + 8), ALIGN), (dict(q=BUF["aq"] + 4), ALIGN),
+    (dict(s=BUF["sa"] + 1), ALIGN),
+    (dict(q=BUF["x"] + 16), ALIAS), (dict(s=BUF["aq"] + 64), ALIAS),
+])
+def test_quantize_rejects(kw, code):
+    assert quant(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), NULL), (dict(y=None), NULL), (dict(M=0), SHAPE),
+    (dict(K=B.QUANT_MAX_K + 128), SHAPE), (dict(ws=None), WORKSPACE),
+    (dict(wsb=100), WORKSPACE), (dict(ws=BUF["ws"] + 128), ALIGN),
+    (dict(x=BUF["x"] + 2), ALIGN), (dict(y=BUF["x"]), ALIAS),
+    (dict(ws=BUF["w"]), ALIAS),
+])
+def test_linear_rejects(kw, code):
+    assert linear(**kw) == code
+
+
+def test_glue_rejects():
+    lib = B.lib()
+    assert lib.w8a8_silu_bf16(None, BUF["out"], 8, None) == NULL
+    assert lib.w8a8_silu_bf16(BUF["x"], BUF["out"], 9, None) == SHAPE
+    assert lib.w8a8_silu_bf16(BUF["x"] + 2, BUF["out"], 8, None) == ALIGN
+    assert lib.w8a8_silu_bf16(BUF["x"], BUF["x"] + 16, 64, None) == ALIAS
+    assert lib.w8a8_pow2_renorm(BUF["x"], BUF["out"], 0, 8, None) == SHAPE
+    assert lib.w8a8_pow2_renorm(BUF["x"], BUF["x"] + 16, 4, 64, None) == ALIAS
+    assert lib.w8a8_quantize_act_silu(BUF["x"], 4, 12, BUF["aq"], BUF["sa"],
+                                      None) == SHAPE
+
+
+def test_no_device_is_reported_without_a_gpu():
+    """Valid arguments on a machine without a GPU: the device check, the
+    last step before any launch, refuses.  Skipped where a GPU exists
+    (there the fake pointers would reach a kernel)."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present")
+    assert gemm() == DEVICE
+    assert quant() == DEVICE
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(B, "LIB_PATH", tmp_path / "missing.so")
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(ImportError):
+        B.lib()

@@ -1,0 +1,299 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bars: INT8 codes, scales, INT32 accumulators and BF16 values are compared
+bit for bit (the kernels follow the oracle's binary32 operation order, so
+FP32 and BF16 outputs are expected exact; FP32 is also checked against the
+1e-6 relative tolerance and BF16 against 1 ulp).  Small shapes span
+several tiles and ragged M / N tails and are checked element by element;
+the full-size DiT blocks are checked on sampled rows (rows are independent
+through quantization, GEMM and SiLU), in the same launch sequence the
+benchmark times.  Outputs sit inside guard regions that must stay intact.
+"""
+from __future__ import annotations
+
+import hashlib
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.pins import ordered
+from w8a8_int8_gemm_amd import binding as B
+from w8a8_int8_gemm_amd import block as BL
+from w8a8_int8_gemm_amd import datagen as D
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+GUARD = 4096  # bytes of canary on each side of an output
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def dev_bf16(bits):
+    return BL.to_device_bf16(bits)
+
+
+def host_bf16(t):
+    return BL.from_device_bf16(t)
+
+
+class Guarded:
+    """A device buffer of `shape`/`dtype` with canary bytes on both sides."""
+
+    def __init__(self, shape, dtype):
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        self.raw = torch.full((GUARD + n + GUARD,), 0xA5, dtype=torch.uint8,
+                              device="cuda")
+        self.t = self.raw[GUARD:GUARD + n].view(dtype).view(*shape)
+
+    def check(self):
+        head = self.raw[:GUARD].cpu().numpy()
+        tail = self.raw[-GUARD:].cpu().numpy()
+        assert np.all(head == 0xA5) and np.all(tail == 0xA5), "guard written"
+
+
+def edge_rows(K: int) -> np.ndarray:
+    """Rows that stress the quantizer: zero, ties, subnormal, signed zero,
+    one outlier, negative maximum."""
+    rows = np.zeros((6, K), np.uint16)
+    f = lambda v: D.to_bf16_bits(np.array(v, np.float32))
+    rows[1, :2] = f([-40.25, 80.5])          # division tie -> -64
+    rows[1, 2:8] = f([127, 2.5, -2.5, 3.5, 0.5, -0.5])
+    rows[2, :3] = np.array([0x0001, 0x8001, 0x0002], np.uint16)  # subnormals
+    rows[3, :] = 0x8000                        # -0
+    rows[3, K // 2] = f([3.0])[0]
+    rows[4, :] = f(np.linspace(-1, 1, K, dtype=np.float32))
+    rows[4, K - 1] = f([1000.0])[0]            # outlier in the tail chunk
+    rows[5, :] = f(-np.abs(np.linspace(0.01, 2, K, dtype=np.float32)))
+    return rows
+
+
+# ---------------------------------------------------------------------------
+# quantization, SiLU, renormalization
+# ---------------------------------------------------------------------------
+
+QUANT_SHAPES = [(1, 8), (3, 128), (65, 5376), (64, 5632), (5, 5640),
+                (7, 21504), (2, 90112), (257, 384), (33, 1000)]
+
+
+@pytest.mark.parametrize("M,K", QUANT_SHAPES)
+def test_quantize_act(orc, M, K):
+    say(f"quantize_act M={M} K={K}")
+    x = D.activations(M, K, seed=100 + M)
+    e = edge_rows(K)
+    x[: min(M, len(e))] = e[: min(M, len(e))]
+    qg = Guarded((M, K), torch.int8)
+    sg = Guarded((M,), torch.float32)
+    B.quantize_act(dev_bf16(x), out=(qg.t, sg.t))
+    torch.cuda.synchronize()
+    q_ref, s_ref = orc.quantize_act(x)
+    q = qg.t.cpu().numpy()
+    s = sg.t.cpu().numpy()
+    qg.check()
+    sg.check()
+    assert np.array_equal(s.view(np.uint32), s_ref.view(np.uint32))
+    bad = np.argwhere(q != q_ref)
+    assert bad.size == 0, f"{len(bad)} codes differ, first {bad[:5].tolist()}"
+
+
+def test_silu_all_bf16_values(orc):
+    say("silu over every finite BF16")
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    b = b[((b >> 7) & 0xFF) != 0xFF]
+    b = b[: len(b) // 8 * 8]
+    y = host_bf16(B.silu(dev_bf16(b)))
+    y_ref = orc.silu_bf16(b)
+    d = np.abs(ordered(y) - ordered(y_ref))
+    assert d.max() <= 1
+    assert np.count_nonzero(d) == 0, f"{np.count_nonzero(d)} differ by 1 ulp"
+
+
+@pytest.mark.parametrize("M,K", [(4, 5376), (3, 21504), (17, 128)])
+def test_quantize_act_silu(orc, M, K):
+    say(f"quantize_act_silu M={M} K={K}")
+    g = np.random.default_rng(M * K)
+    x = D.to_bf16_bits((g.standard_normal((M, K)) * 30).astype(np.float32))
+    xd = dev_bf16(x)
+    q, s = B.quantize_act(xd, silu=True)
+    h = B.silu(xd)
+    torch.cuda.synchronize()
+    h_ref = orc.silu_bf16(x)
+    assert np.array_equal(host_bf16(h), h_ref)
+    q_ref, s_ref = orc.quantize_act(h_ref)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32),
+                          s_ref.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+@pytest.mark.parametrize("M,K", [(6, 5376), (9, 21504), (5, 8)])
+def test_pow2_renorm(orc, M, K):
+    say(f"pow2_renorm M={M} K={K}")
+    x = D.activations(M, K, seed=7)
+    x[0] = 0
+    x[1, :3] = [0x0001, 0x8003, 0x0002]
+    x[1, 3:] = 0
+    x[2] = D.to_bf16_bits(np.full(K, 3e38, np.float32))
+    y = host_bf16(B.pow2_renorm(dev_bf16(x)))
+    assert np.array_equal(y, orc.pow2_renorm(x))
+
+
+# ---------------------------------------------------------------------------
+# GEMM
+# ---------------------------------------------------------------------------
+
+GEMM_SHAPES = [(1, 128, 128), (3, 384, 256), (64, 5376, 5376),
+               (65, 256, 384), (257, 1280, 2048), (300, 384, 1152),
+               (513, 768, 640), (1000, 640, 256)]
+
+
+def gemm_inputs(M, N, K, seed):
+    g = np.random.default_rng([seed, M, N, K])
+    a = g.integers(-128, 128, (M, K), dtype=np.int8)
+    w = g.integers(-128, 128, (N, K), dtype=np.int8)
+    sa = np.exp(g.normal(-4, 2, M)).astype(np.float32)
+    sa[0] = 0.0
+    sw = np.exp(g.normal(-6, 0.3, N)).astype(np.float32)
+    bias = D.to_bf16_bits(g.normal(0, 0.02, N).astype(np.float32))
+    return a, w, sa, sw, bias
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_i32(orc, M, N, K):
+    say(f"gemm I32 M={M} N={N} K={K} workspace={B.workspace_bytes(M, N, K)}")
+    a, w, sa, sw, bias = gemm_inputs(M, N, K, 1)
+    og = Guarded((M, N), torch.int32)
+    B.gemm(dev(a), dev(sa), dev(w), dev(sw), dev_bf16(bias),
+           out_dtype=torch.int32, out=og.t)
+    torch.cuda.synchronize()
+    got = og.t.cpu().numpy()
+    og.check()
+    want = orc.gemm_i32(a, w)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} accumulators differ: {bad[:5].tolist()}"
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_gemm_fp32_bf16(orc, M, N, K, with_bias):
+    say(f"gemm FP32/BF16 M={M} N={N} K={K} bias={with_bias}")
+    a, w, sa, sw, bias = gemm_inputs(M, N, K, 2)
+    bias_h = bias if with_bias else None
+    args = (dev(a), dev(sa), dev(w), dev(sw),
+            dev_bf16(bias) if with_bias else None)
+    fg = Guarded((M, N), torch.float32)
+    bg = Guarded((M, N), torch.bfloat16)
+    B.gemm(*args, out_dtype=torch.float32, out=fg.t)
+    B.gemm(*args, out_dtype=torch.bfloat16, out=bg.t)
+    torch.cuda.synchronize()
+    yf = fg.t.cpu().numpy()
+    yb = host_bf16(bg.t)
+    fg.check()
+    bg.check()
+    rf, rb = orc.epilogue(orc.gemm_i32(a, w), sa, sw, bias_h)
+    # contract tolerances
+    rel = np.abs(yf.astype(np.float64) - rf) / np.maximum(np.abs(rf), 1e-300)
+    assert np.all((rel <= 1e-6) | (yf == rf))
+    assert np.abs(ordered(yb) - ordered(rb)).max() <= 1
+    # the kernel follows the oracle's operation order: exact
+    assert np.array_equal(yf.view(np.uint32), rf.view(np.uint32))
+    assert np.array_equal(yb, rb)
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 5376, 5376), (129, 384, 640),
+                                   (1, 256, 21504)])
+def test_linear(orc, M, N, K):
+    say(f"linear M={M} N={N} K={K}")
+    x = D.activations(M, K, seed=3)
+    w = D.weights(N, K, seed=3)
+    sw = D.weight_scales(N, seed=3)
+    b = D.bias(N, seed=3)
+    yg = Guarded((M, N), torch.bfloat16)
+    B.linear(dev_bf16(x), dev(w), dev(sw), dev_bf16(b), out=yg.t)
+    torch.cuda.synchronize()
+    y = host_bf16(yg.t)
+    yg.check()
+    assert np.array_equal(y, orc.linear(x, w, sw, b))
+
+
+def test_gemm_deterministic():
+    say("gemm determinism")
+    M, N, K = 4096, 5376, 5376
+    a, w, sa, sw, bias = gemm_inputs(M, N, K, 9)
+    args = (dev(a), dev(sa), dev(w), dev(sw), dev_bf16(bias))
+    h = []
+    for _ in range(2):
+        y = B.gemm(*args)
+        torch.cuda.synchronize()
+        h.append(hashlib.sha256(host_bf16(y).tobytes()).hexdigest())
+    assert h[0] == h[1]
+
+
+# ---------------------------------------------------------------------------
+# full-size DiT blocks, sampled rows
+# ---------------------------------------------------------------------------
+
+def oracle_block_rows(orc, x_rows, params):
+    """Oracle of the block's data flow on a subset of token rows."""
+    out = {}
+    q, s = orc.quantize_act(x_rows)
+    out["xq"], out["xs"] = q, s
+    for n in ("q", "k", "v", "o", "fc1"):
+        p = params[n]
+        out[n] = orc.linear(x_rows, p.w, p.sw, p.bias)
+    h = orc.silu_bf16(out["fc1"])
+    out["hq"], out["hs"] = orc.quantize_act(h)
+    p = params["fc2"]
+    out["fc2"] = orc.linear(h, p.w, p.sw, p.bias)
+    return out
+
+
+def test_config0_single_projection(orc):
+    wl = D.WORKLOADS[0]
+    say(f"config 0: {wl.name} M={wl.M}, every output checked")
+    p = wl.projs[0]
+    pp = D.proj_params(p, wl.seed)
+    x = D.activations(wl.M, p.K, wl.seed)
+    q, s = B.quantize_act(dev_bf16(x))
+    y = B.gemm(q, s, dev(pp.w), dev(pp.sw), dev_bf16(pp.bias))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16(y), orc.linear(x, pp.w, pp.sw, pp.bias))
+
+
+@pytest.mark.parametrize("config", [1, 2, 3])
+def test_block_sampled_rows(orc, config):
+    wl = D.WORKLOADS[config]
+    say(f"block config {config}: {wl.name} M={wl.M}")
+    params = D.block_params(wl, 0)
+    projs = {p.name: BL.upload_proj(p, params[p.name]) for p in wl.projs}
+    x = D.activations(wl.M, D.HIDDEN, wl.seed)
+    runner = BL.BlockRunner(wl.M)
+    out = runner.run(dev_bf16(x), projs)
+    torch.cuda.synchronize()
+    rows = D.row_sample(wl.M, 24, wl.seed)
+    ri = torch.from_numpy(rows).cuda()
+    ref = oracle_block_rows(orc, x[rows], params)
+    assert np.array_equal(runner.xq[0][ri].cpu().numpy(), ref["xq"])
+    assert np.array_equal(runner.xs[0][ri].cpu().numpy().view(np.uint32),
+                          ref["xs"].view(np.uint32))
+    for n in ("q", "k", "v", "o", "fc1"):
+        got = host_bf16(out[n][ri])
+        assert np.array_equal(got, ref[n]), n
+    assert np.array_equal(runner.hq[ri].cpu().numpy(), ref["hq"])
+    assert np.array_equal(runner.hs[ri].cpu().numpy().view(np.uint32),
+                          ref["hs"].view(np.uint32))
+    assert np.array_equal(host_bf16(out["fc2"][ri]), ref["fc2"])

@@ -1,0 +1,217 @@
+"""Python binding of libw8a8.so (include/w8a8.h): argument marshalling only.
+
+Torch tensors supply device memory and the current HIP stream; every step
+of the computation runs in the library's HIP kernels.  Loading fails loudly
+when the shared object is missing: there is no CPU or PyTorch fallback.
+
+BF16 tensors are passed as their bit patterns (the library's uint16 BF16).
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+LIB_PATH = PKG / "libw8a8.so"
+
+OUT_BF16, OUT_FP32, OUT_I32 = 0, 1, 2
+W8A8_OK = 0
+STATUS = {
+    0: "W8A8_OK", 1: "W8A8_ERR_NULL", 2: "W8A8_ERR_SHAPE",
+    3: "W8A8_ERR_ALIGN", 4: "W8A8_ERR_WORKSPACE", 5: "W8A8_ERR_OUT_DTYPE",
+    6: "W8A8_ERR_ALIAS", 7: "W8A8_ERR_DEVICE", 8: "W8A8_ERR_HIP",
+}
+MAX_K = 130944
+QUANT_MAX_K = 90112
+
+# Every symbol include/w8a8.h declares, with its ctypes signature.
+_P, _I64, _SZ, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+SIGNATURES = {
+    "w8a8_quantize_act": (_I, [_P, _I64, _I64, _P, _P, _P]),
+    "w8a8_quantize_act_silu": (_I, [_P, _I64, _I64, _P, _P, _P]),
+    "w8a8_gemm": (_I, [_P, _P, _P, _P, _P, _P, _I, _I64, _I64, _I64, _P,
+                       _SZ, _P]),
+    "w8a8_linear": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ,
+                         _P]),
+    "w8a8_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "w8a8_linear_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "w8a8_status_string": (ctypes.c_char_p, [_I]),
+    "w8a8_last_hip_error": (_I, []),
+    "w8a8_silu_bf16": (_I, [_P, _P, _I64, _P]),
+    "w8a8_pow2_renorm": (_I, [_P, _P, _I64, _I64, _P]),
+}
+
+
+class W8A8Error(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str = ""):
+        self.status = status
+        super().__init__(f"{fn}: {STATUS.get(status, status)} "
+                         f"({lib().w8a8_status_string(status).decode()})"
+                         f"{detail}")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded shared object (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m w8a8_int8_gemm_amd.build` (or "
+                "__graft_entry__.build()); there is no fallback path")
+        L = ctypes.CDLL(str(LIB_PATH))
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != W8A8_OK:
+        detail = ""
+        if status == 8:
+            detail = f" hipError={lib().w8a8_last_hip_error()}"
+        raise W8A8Error(fn, status, detail)
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrappers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, dtype, ndim, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype or t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {dtype} with {ndim} "
+                         f"dims, got {t.dtype} {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+
+
+def quantize_act(x, *, silu: bool = False, out=None, stream=None):
+    """x: bf16 [M,K] -> (a_q int8 [M,K], a_scale float32 [M]).
+    silu=True applies SiLU (rounded to BF16) before quantizing."""
+    torch = _torch()
+    _need(x, torch.bfloat16, 2, "x")
+    M, K = x.shape
+    if out is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        s = torch.empty((M,), dtype=torch.float32, device=x.device)
+    else:
+        q, s = out
+    fn = lib().w8a8_quantize_act_silu if silu else lib().w8a8_quantize_act
+    _check("w8a8_quantize_act" + ("_silu" if silu else ""),
+           fn(_ptr(x), M, K, _ptr(q), _ptr(s), _stream(stream)))
+    return q, s
+
+
+def workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().w8a8_workspace_bytes(M, N, K))
+
+
+def linear_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().w8a8_linear_workspace_bytes(M, N, K))
+
+
+def _workspace(nbytes, device, given=None):
+    torch = _torch()
+    if given is not None:
+        return given
+    if nbytes == 0:
+        return None
+    return torch.empty((nbytes,), dtype=torch.uint8, device=device)
+
+
+def gemm(a_q, a_scale, w_q, w_scale, bias=None, out_dtype=None, *, out=None,
+         workspace=None, stream=None):
+    """INT8 GEMM + fused epilogue.  out_dtype: torch.bfloat16 (default),
+    torch.float32 (epilogue before rounding) or torch.int32 (accumulators).
+    """
+    torch = _torch()
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    codes = {torch.bfloat16: OUT_BF16, torch.float32: OUT_FP32,
+             torch.int32: OUT_I32}
+    if out_dtype not in codes:
+        raise ValueError(f"out_dtype {out_dtype} not supported")
+    _need(a_q, torch.int8, 2, "a_q")
+    _need(a_scale, torch.float32, 1, "a_scale")
+    _need(w_q, torch.int8, 2, "w_q")
+    _need(w_scale, torch.float32, 1, "w_scale")
+    if bias is not None:
+        _need(bias, torch.bfloat16, 1, "bias")
+    M, K = a_q.shape
+    N = w_q.shape[0]
+    if w_q.shape[1] != K:
+        raise ValueError("a_q and w_q disagree on K")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
+    ws_need = workspace_bytes(M, N, K)
+    ws = _workspace(ws_need, a_q.device, workspace)
+    ws_len = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("w8a8_gemm", lib().w8a8_gemm(
+        _ptr(a_q), _ptr(a_scale), _ptr(w_q), _ptr(w_scale), _ptr(bias),
+        _ptr(out), codes[out_dtype], M, N, K, _ptr(ws), ws_len,
+        _stream(stream)))
+    return out
+
+
+def linear(x, w_q, w_scale, bias=None, *, out=None, workspace=None,
+           stream=None):
+    """y = bf16(((float)(quant(x) . w_q^T) * sa) * sw + bias)."""
+    torch = _torch()
+    _need(x, torch.bfloat16, 2, "x")
+    _need(w_q, torch.int8, 2, "w_q")
+    _need(w_scale, torch.float32, 1, "w_scale")
+    if bias is not None:
+        _need(bias, torch.bfloat16, 1, "bias")
+    M, K = x.shape
+    N = w_q.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    ws = _workspace(linear_workspace_bytes(M, N, K), x.device, workspace)
+    ws_len = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("w8a8_linear", lib().w8a8_linear(
+        _ptr(x), _ptr(w_q), _ptr(w_scale), _ptr(bias), _ptr(out), M, N, K,
+        _ptr(ws), ws_len, _stream(stream)))
+    return out
+
+
+def silu(x, *, out=None, stream=None):
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or not x.is_contiguous() or not x.is_cuda:
+        raise ValueError("x must be a contiguous bf16 GPU tensor")
+    y = torch.empty_like(x) if out is None else out
+    _check("w8a8_silu_bf16", lib().w8a8_silu_bf16(
+        _ptr(x), _ptr(y), x.numel(), _stream(stream)))
+    return y
+
+
+def pow2_renorm(x, *, out=None, stream=None):
+    torch = _torch()
+    _need(x, torch.bfloat16, 2, "x")
+    M, K = x.shape
+    y = torch.empty_like(x) if out is None else out
+    _check("w8a8_pow2_renorm", lib().w8a8_pow2_renorm(
+        _ptr(x), _ptr(y), M, K, _stream(stream)))
+    return y
