@@ -297,3 +297,42 @@ def test_block_sampled_rows(orc, config):
     assert np.array_equal(runner.hs[ri].cpu().numpy().view(np.uint32),
                           ref["hs"].view(np.uint32))
     assert np.array_equal(host_bf16(out["fc2"][ri]), ref["fc2"])
+
+
+def test_gemm_epilogue_edge_values(orc):
+    """Accumulators, scales and biases chosen to hit BF16 ties, results
+    that are FP32/BF16 subnormal, the bias-before-rounding case and
+    negative values; rows carry the accumulator (row m of A has acc[m]
+    entries equal to +-1, every weight is 1), columns the weight scale and
+    bias.  Checked exactly against the oracle on every (row, column) pair,
+    through both the staged large-M kernel and the skinny split-K path."""
+    K = 1152
+    accs = [257, 258, 259, -257, 0, 1, -1, 1000, 1024, K, -K, 3, 515, 771]
+    sas = [1.0, 1.0, 1.0, 1.0, 1.0, 2.0 ** -140, 2.0 ** -140, 0.5, 2.0 ** -126,
+           1.0, 1.0, 0.375, 2.0 ** -7, 1.0]
+    sws = [1.0, 0.25, 2.0 ** -9, 0.5, 1.0, 2.0 ** 3] * 43
+    biases = [0.0, 0.5, -0.25, 0.0, 2.0 ** -133, 1.0] * 43
+    N = 256
+    sws, biases = sws[:N], biases[:N]
+    for M in (300, 14):   # 300 rows: large-M kernel; 14 rows: split-K path
+        say(f"gemm epilogue edge values M={M} N={N} K={K}")
+        a = np.zeros((M, K), np.int8)
+        sa = np.zeros(M, np.float32)
+        for m in range(M):
+            v = accs[m % len(accs)]
+            a[m, : abs(v)] = 1 if v > 0 else -1
+            sa[m] = sas[m % len(sas)]
+        w = np.ones((N, K), np.int8)
+        sw = np.array(sws, np.float32)
+        bias = D.to_bf16_bits(np.array(biases, np.float32))
+        y = B.gemm(dev(a), dev(sa), dev(w), dev(sw), dev_bf16(bias))
+        yf = B.gemm(dev(a), dev(sa), dev(w), dev(sw), dev_bf16(bias),
+                    out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        rf, rb = orc.epilogue(orc.gemm_i32(a, w), sa, sw, bias)
+        assert np.array_equal(yf.cpu().numpy().view(np.uint32),
+                              rf.view(np.uint32))
+        got = host_bf16(y)
+        bad = np.argwhere(got != rb)
+        assert bad.size == 0, (f"{len(bad)} differ, first "
+                               f"{[(int(i), int(j), hex(got[i, j]), hex(rb[i, j])) for i, j in bad[:4]]}")

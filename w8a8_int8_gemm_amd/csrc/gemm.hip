@@ -33,6 +33,8 @@
 //     are exact in any order) and applies the epilogue.
 #include "internal.h"
 
+#include <type_traits>
+
 #pragma clang fp contract(off)
 
 namespace w8a8 {
@@ -47,7 +49,8 @@ typedef __attribute__((address_space(1))) void gbl_void;
 constexpr int kXcds = 8;
 constexpr int EPI_PARTIAL = 3;  // split-K slice: raw INT32 to the workspace
 
-template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int GROUP_M_>
+template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int GROUP_M_,
+          int NS_>
 struct Cfg {
   static constexpr int BM = BM_;   // tokens per block tile
   static constexpr int BN = BN_;   // output channels per block tile
@@ -55,6 +58,7 @@ struct Cfg {
   static constexpr int WGM = WGM_; // waves along M
   static constexpr int WGN = WGN_; // waves along N
   static constexpr int GROUP_M = GROUP_M_;
+  static constexpr int NS = NS_;   // LDS stages in the ring (NS-1 in flight)
   static constexpr int WAVES = WGM * WGN;
   static constexpr int THREADS = WAVES * 64;
   static constexpr int WM = BM / WGM;  // tokens per wave
@@ -65,7 +69,11 @@ struct Cfg {
   static constexpr int A_BYTES = BM * BK;
   static constexpr int B_BYTES = BN * BK;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int LDS = NS * STAGE;
+  static constexpr int KS = BK / 32;  // MFMA k-steps per stage
+  // BF16 epilogue staged through LDS (needs 128-channel waves and room for
+  // the whole BM x BN BF16 tile in the ring).
+  static constexpr bool STAGED_EPI = (WN == 128) && (BM * BN * 2 <= LDS);
   static constexpr int A_LOADS = A_BYTES / (1024 * WAVES);  // per wave
   static constexpr int B_LOADS = B_BYTES / (1024 * WAVES);
   static_assert(BK == 64 || BK == 128, "BK");
@@ -73,6 +81,12 @@ struct Cfg {
   static_assert(A_BYTES % (1024 * WAVES) == 0, "A staging");
   static_assert(B_BYTES % (1024 * WAVES) == 0, "B staging");
   static_assert(LDS <= 160 * 1024, "LDS");
+  // Stage kt+1 must already be requested when the wave waits for it at the
+  // end of stage kt, so the ring needs at least 3 slots.
+  static_assert(NS >= 3 && NS <= 6, "stages");
+  static_assert((A_BYTES + B_BYTES) / (1024 * WAVES) * (NS - 2) <= 63,
+                "vmcnt counts at most 63 outstanding loads");
+  static_assert(KS % 2 == 0, "fragment double buffering alternates per k-step");
 };
 
 // Position of logical 16-byte chunk c in LDS row r (an involution in c).
@@ -90,6 +104,18 @@ __device__ __forceinline__ v4i read_lds16(const int8_t *lds_base, int off) {
   return *reinterpret_cast<const v4i *>(lds_base + off);
 }
 
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+
+// Two binary32 values -> two BF16 (round to nearest, ties to even) packed in
+// one dword, low half first: gfx950's v_cvt_pk_bf16_f32.  The epilogue's
+// values are finite or +-Inf (finite scales and activations are a
+// documented precondition), never NaN.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf2v b = __builtin_convertvector(f2v{lo, hi}, bf2v);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
 // Block id -> (token tile, channel tile).
 __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n,
                                         int group_m, int &tm, int &tn) {
@@ -105,6 +131,56 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n,
   const int within = L - g * span;
   tm = first + within % gsize;
   tn = within / gsize;
+}
+
+// Wait until this wave's direct loads of one stage have landed in LDS.
+// Loads complete in issue order, so it suffices that no more than the loads
+// of the `later` stages requested after it remain outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// s_waitcnt immediate for gfx9-family: vmcnt in bits [3:0] and [15:14],
+// expcnt [6:4], lgkmcnt [11:8]; unconstrained counters at their maximum.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 0xF) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
+}
+
+// Wait until at most N LDS reads of this wave are outstanding.  The builtin
+// (rather than inline asm) lets the compiler's own wait insertion see it;
+// the scheduling barriers keep the surrounding reads and MFMAs in order.
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt");
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, N));
+}
+
+template <int LOADS, int NS>
+__device__ __forceinline__ void wait_stage_landed(int later) {
+  // at most NS-2 stages are ever in flight behind the one waited for
+  if constexpr (NS - 2 >= 4) {
+    if (later >= 4) { wait_vmcnt<4 * LOADS>(); return; }
+  }
+  if constexpr (NS - 2 >= 3) {
+    if (later == 3) { wait_vmcnt<3 * LOADS>(); return; }
+  }
+  if constexpr (NS - 2 >= 2) {
+    if (later == 2) { wait_vmcnt<2 * LOADS>(); return; }
+  }
+  if constexpr (NS - 2 >= 1) {
+    if (later == 1) { wait_vmcnt<LOADS>(); return; }
+  }
+  wait_vmcnt<0>();
+}
+
+// Workgroup barrier without the memory fences of __syncthreads (which would
+// also wait for every outstanding direct load); ordering of LDS data is
+// handled by the explicit vmcnt waits above.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 struct KernelArgs {
@@ -141,44 +217,70 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(KernelArgs p) {
   const int kt1 = (int)((int64_t)(z + 1) * p.stages_total / p.splits);
   const int nk = kt1 - kt0;
 
-  // Per-lane global source of each direct load (stage 0 of this split).
-  const int8_t *ga[C::A_LOADS];
-  const int8_t *gb[C::B_LOADS];
+  // Direct loads: a uniform base per operand, advanced by BK bytes per
+  // stage, plus a 32-bit per-lane offset per load instruction (the row in
+  // the tile, clamped to the last valid row, times K, plus the chunk that
+  // lands in this lane's 16 LDS bytes).  Row offsets stay below
+  // 256 * W8A8_MAX_K < 2^31.
+  const int8_t *a_base = p.a + (int64_t)m0 * p.K + (int64_t)kt0 * C::BK;
+  const int8_t *b_base = p.w + (int64_t)n0 * p.K + (int64_t)kt0 * C::BK;
+  int oa[C::A_LOADS], ob[C::B_LOADS];
 #pragma unroll
   for (int j = 0; j < C::A_LOADS; ++j) {
     const int slot = (j * C::WAVES + wave) * 64 + lane;
     const int r = slot / C::CPR;
     const int c = swz<C::CPR>(r, slot % C::CPR);
-    const int row = min(m0 + r, p.M - 1);
-    ga[j] = p.a + (int64_t)row * p.K + (int64_t)kt0 * C::BK + c * 16;
+    oa[j] = min(r, p.M - 1 - m0) * p.K + c * 16;
   }
 #pragma unroll
   for (int j = 0; j < C::B_LOADS; ++j) {
     const int slot = (j * C::WAVES + wave) * 64 + lane;
     const int r = slot / C::CPR;
     const int c = swz<C::CPR>(r, slot % C::CPR);
-    const int row = min(n0 + r, p.N - 1);
-    gb[j] = p.w + (int64_t)row * p.K + (int64_t)kt0 * C::BK + c * 16;
+    ob[j] = min(r, p.N - 1 - n0) * p.K + c * 16;
   }
 
-  auto issue = [&](int stage_idx, int buf) {
-    int8_t *sa_base = smem + buf * C::STAGE;
+  // Request stage `src` of this split into ring slot `slot`.
+  auto issue_into = [&](int slot, int src) {
+    const int stage_idx = src;
+    int8_t *sa_base = smem + slot * C::STAGE;
     int8_t *sb_base = sa_base + C::A_BYTES;
-    const int64_t koff = (int64_t)stage_idx * C::BK;
+    const int8_t *ga = a_base + (int64_t)stage_idx * C::BK;
+    const int8_t *gb = b_base + (int64_t)stage_idx * C::BK;
 #pragma unroll
     for (int j = 0; j < C::A_LOADS; ++j)
-      load_lds16(ga[j] + koff,
+      load_lds16(ga + oa[j],
                  (lds_void *)(sa_base + (j * C::WAVES + wave) * 1024));
 #pragma unroll
     for (int j = 0; j < C::B_LOADS; ++j)
-      load_lds16(gb[j] + koff,
+      load_lds16(gb + ob[j],
                  (lds_void *)(sb_base + (j * C::WAVES + wave) * 1024));
   };
 
-  // Fragment read offsets (bytes within a tile) for k-step 0; the k-step
-  // adds 2 chunks, which the swizzle maps with a per-row XOR.
+  // Fragment reads: lane reads 16 bytes of row (lane & 31) of each 32-row
+  // fragment, logical chunk 2*ks + (lane >> 5) of the stage, at its swizzled
+  // position.  Fragment rows start at multiples of 32, where the swizzle
+  // repeats, so one per-lane offset per k-step serves every fragment.
   const int frow = lane & 31;
   const int fchunk = lane >> 5;
+  int rx[C::KS], rw[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    const int r1 = wave_m * C::WM + frow;
+    const int r2 = wave_n * C::WN + frow;
+    rx[ks] = r1 * C::BK + swz<C::CPR>(r1, ks * 2 + fchunk) * 16;
+    rw[ks] = C::A_BYTES + r2 * C::BK + swz<C::CPR>(r2, ks * 2 + fchunk) * 16;
+  }
+  v4i fx[2][C::TM], fw[2][C::TN];
+  auto read_frags = [&](int buf, int ks, v4i *xa, v4i *wb) {
+    const int8_t *base = smem + buf * C::STAGE;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+      xa[i] = read_lds16(base, rx[ks] + i * 32 * C::BK);
+#pragma unroll
+    for (int i = 0; i < C::TN; ++i)
+      wb[i] = read_lds16(base, rw[ks] + i * 32 * C::BK);
+  };
 
   v16i acc[C::TN][C::TM];
 #pragma unroll
@@ -188,39 +290,150 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(KernelArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-  if (nk > 0) issue(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
-    const int8_t *sa_base = smem + (kt & 1) * C::STAGE;
-    const int8_t *sb_base = sa_base + C::A_BYTES;
+  // Ring of NS stages: stages 0..NS-2 are requested up front; at the end of
+  // stage kt the wave waits until stage kt+1 has landed (the later stages
+  // may stay in flight), all waves meet at a barrier (so every read of
+  // stage kt-1's slot is done), and stage kt+NS-1 is requested into that
+  // slot.  Fragment registers are double buffered across k-steps: the
+  // reads of k-step s+1 are interleaved with the MFMAs of k-step s.
+  // While stage kt+NS-1 exists (the steady state) the number of stages in
+  // flight behind stage kt+1 is the constant NS-3, so the steady-state loop
+  // body is straight-line code; the last NS-2 stages drain separately.
+  constexpr int LOADS = C::A_LOADS + C::B_LOADS;  // per wave per stage
+  constexpr int READS = C::TM + C::TN;            // per k-step per wave
+  constexpr int MFMAS = C::TM * C::TN;            // per k-step per wave
+  auto mfma_step = [&](const v4i *xa, const v4i *wb) {
 #pragma unroll
-    for (int ks = 0; ks < C::BK / 32; ++ks) {
-      v4i xa[C::TM], wb[C::TN];
+    for (int i = 0; i < C::TN; ++i)
 #pragma unroll
-      for (int i = 0; i < C::TM; ++i) {
-        const int r = wave_m * C::WM + i * 32 + frow;
-        xa[i] = read_lds16(sa_base,
-                           r * C::BK + swz<C::CPR>(r, ks * 2 + fchunk) * 16);
-      }
+      for (int j = 0; j < C::TM; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wb[i], xa[j],
+                                                          acc[i][j], 0, 0, 0);
+  };
+  // Interleave: after every MFMAS/READS MFMAs, one fragment read.
+  auto interleave = [&]() {
+#ifndef W8A8_NO_INTERLEAVE_HINTS
 #pragma unroll
-      for (int i = 0; i < C::TN; ++i) {
-        const int r = wave_n * C::WN + i * 32 + frow;
-        wb[i] = read_lds16(sb_base,
-                           r * C::BK + swz<C::CPR>(r, ks * 2 + fchunk) * 16);
-      }
-#pragma unroll
-      for (int i = 0; i < C::TN; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wb[i], xa[j],
-                                                            acc[i][j], 0, 0, 0);
+    for (int r = 0; r < READS; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, MFMAS / READS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    if constexpr (MFMAS % READS != 0)
+      __builtin_amdgcn_sched_group_barrier(0x008, MFMAS % READS, 0);
+#endif
+  };
+  // One stage: its KS k-steps; the last one crosses into stage kt+1.
+  // Every stage but the last requests one stage's loads after its barrier:
+  // stage kt+NS-1 while it exists, otherwise a second copy of the last
+  // stage into the free slot (harmless, and it keeps the number of loads in
+  // flight behind stage kt+1 at the constant NS-3 stages, so the loop has
+  // one body and one wait count).
+  auto stage = [&](int kt, bool last) {
+    const int buf = kt % C::NS;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const int cur = ks & 1;
+      // Code does not move across k-steps: that would keep three fragment
+      // sets live and spill.
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks + 1 < C::KS) {
+        read_frags(buf, ks + 1, fx[cur ^ 1], fw[cur ^ 1]);
+        mfma_step(fx[cur], fw[cur]);
+        interleave();
+      } else if (!last) {
+        wait_vmcnt<(C::NS - 3) * LOADS>();
+        block_barrier();
+        issue_into((kt + C::NS - 1) % C::NS, min(kt + C::NS - 1, nk - 1));
+        read_frags((kt + 1) % C::NS, 0, fx[cur ^ 1], fw[cur ^ 1]);
+        mfma_step(fx[cur], fw[cur]);
+        interleave();
+      } else {
+        mfma_step(fx[cur], fw[cur]);
+      }
+    }
+  };
+  // Prologue: stages 0..NS-2 (a missing stage is replaced by a copy of the
+  // last one, as above), then wait for stage 0.
+  // (The host plans at least 8 stages per split; a split without stages
+  // skips the pipeline and stores zero accumulators.)
+  if (nk > 0) {
+#pragma unroll
+    for (int s = 0; s < C::NS - 1; ++s) issue_into(s, min(s, nk - 1));
+    wait_vmcnt<(C::NS - 2) * LOADS>();
+    block_barrier();
+    read_frags(0, 0, fx[0], fw[0]);
+    for (int kt = 0; kt + 1 < nk; ++kt) stage(kt, false);
+    stage(nk - 1, true);
   }
 
   // Epilogue.  Lane holds token m = base + (lane & 31) and, for register
   // 4g + t, channel n = base + 8g + 4*(lane >> 5) + t.
+  if constexpr (EPI == EPI_BF16 && C::STAGED_EPI) {
+    // BF16 results go through LDS so that the global stores write whole
+    // row segments (16 lanes x 16 B = 256 contiguous bytes per row) rather
+    // than 32 rows x 16 B per instruction.  Each wave stages its WM x WN
+    // block row-major in its own LDS region; 16-byte chunk c of row r sits
+    // at chunk c ^ (r mod CPRW) and its 8-byte halves are swapped when bit 4
+    // of r is set, which keeps both the 8-byte writes (32 rows per half
+    // wave) and the 16-byte reads free of bank conflicts.
+    constexpr int ROWB = C::WN * 2;    // bytes per staged row
+    constexpr int CPRW = ROWB / 16;    // 16-byte chunks per staged row
+    constexpr int RPI = 64 / CPRW;     // staged rows per wave read
+    wait_vmcnt<0>();  // every direct load, including drain copies, landed
+    block_barrier();  // and every wave is done reading the ring
+    int8_t *region = smem + wave * (C::WM * ROWB);
+    const int mb = m0 + wave_m * C::WM;
+    const int nb = n0 + wave_n * C::WN;
+    const bool has_bias = p.bias != nullptr;
+#pragma unroll
+    for (int j = 0; j < C::TM; ++j) {
+      const int r = j * 32 + (lane & 31);
+      const int m = mb + r;
+      const float sam = m < p.M ? p.sa[m] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < C::TN; ++i) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int nl = i * 32 + 8 * g + 4 * (lane >> 5);
+          const int n = nb + nl;
+          uint2 v = make_uint2(0, 0);
+          if (n < p.N) {
+            const float4 swn = *reinterpret_cast<const float4 *>(p.sw + n);
+            float t0 = ((float)acc[i][j][4 * g + 0] * sam) * swn.x;
+            float t1 = ((float)acc[i][j][4 * g + 1] * sam) * swn.y;
+            float t2 = ((float)acc[i][j][4 * g + 2] * sam) * swn.z;
+            float t3 = ((float)acc[i][j][4 * g + 3] * sam) * swn.w;
+            if (has_bias) {
+              const uint2 b = *reinterpret_cast<const uint2 *>(p.bias + n);
+              t0 = t0 + bf16_to_f32(b.x & 0xFFFFu);
+              t1 = t1 + bf16_to_f32(b.x >> 16);
+              t2 = t2 + bf16_to_f32(b.y & 0xFFFFu);
+              t3 = t3 + bf16_to_f32(b.y >> 16);
+            }
+            v.x = pack_bf16x2(t0, t1);
+            v.y = pack_bf16x2(t2, t3);
+          }
+          const int c = nl >> 3, h = (nl >> 2) & 1;
+          const int off = r * ROWB + ((c ^ (r & (CPRW - 1))) << 4) +
+                          ((h ^ ((r >> 4) & 1)) << 3);
+          *reinterpret_cast<uint2 *>(region + off) = v;
+        }
+      }
+    }
+    uint16_t *out = static_cast<uint16_t *>(p.out);
+#pragma unroll 4
+    for (int it = 0; it < C::WM / RPI; ++it) {
+      const int r = it * RPI + lane / CPRW;
+      const int c = lane % CPRW;
+      v4i v = *reinterpret_cast<const v4i *>(region + r * ROWB +
+                                             ((c ^ (r & (CPRW - 1))) << 4));
+      if ((r >> 4) & 1) v = v4i{v.z, v.w, v.x, v.y};
+      const int m = mb + r, n = nb + c * 8;
+      if (m < p.M && n < p.N)
+        *reinterpret_cast<v4i *>(out + (int64_t)m * p.N + n) = v;
+    }
+    return;
+  }
   const int64_t MN = (int64_t)p.M * p.N;
 #pragma unroll
   for (int j = 0; j < C::TM; ++j) {
@@ -259,8 +472,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(KernelArgs p) {
               make_float4(t0, t1, t2, t3);
         } else {
           uint2 v;
-          v.x = f32_to_bf16_rne(t0) | (f32_to_bf16_rne(t1) << 16);
-          v.y = f32_to_bf16_rne(t2) | (f32_to_bf16_rne(t3) << 16);
+          v.x = pack_bf16x2(t0, t1);
+          v.y = pack_bf16x2(t2, t3);
           *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.out) + o) = v;
         }
       }
@@ -306,8 +519,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
           make_float4(t0, t1, t2, t3);
     } else {
       uint2 v;
-      v.x = f32_to_bf16_rne(t0) | (f32_to_bf16_rne(t1) << 16);
-      v.y = f32_to_bf16_rne(t2) | (f32_to_bf16_rne(t3) << 16);
+      v.x = pack_bf16x2(t0, t1);
+      v.y = pack_bf16x2(t2, t3);
       *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + o) = v;
     }
   }
@@ -316,11 +529,25 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
 // ---------------------------------------------------------------------------
 // Tile configurations
 // ---------------------------------------------------------------------------
-using CfgLarge = Cfg<256, 256, 64, 2, 2, 8>;   // large M: 4 waves, 128x128 each
-using CfgSkinny = Cfg<64, 128, 64, 1, 4, 1>;   // small M: 4 waves, 64x32 each
+// Large M: 256x256 tiles, 8 waves (two per SIMD) of 64x128, 4-stage ring
+// of 64-byte K stages (128 KiB LDS).  Small M: 64x128 tiles, 4 waves of 64x32.
+#ifndef W8A8_CFG_LARGE
+#define W8A8_CFG_LARGE 256, 256, 64, 4, 2, 4, 4
+#endif
+#ifndef W8A8_CFG_SKINNY
+#define W8A8_CFG_SKINNY 64, 128, 64, 1, 4, 1, 4
+#endif
+using CfgLarge = Cfg<W8A8_CFG_LARGE>;
+using CfgSkinny = Cfg<W8A8_CFG_SKINNY>;
+
+template <class C>
+hipError_t set_lds_limit();
 
 template <class C>
 hipError_t launch_cfg(const GemmArgs &g, int splits, hipStream_t stream) {
+  // Dynamic LDS above 64 KiB needs an explicit opt-in, once per process.
+  static const hipError_t lds_ok = set_lds_limit<C>();
+  if (lds_ok != hipSuccess) return lds_ok;
   KernelArgs p;
   p.a = g.a;
   p.sa = g.sa;
