@@ -53,7 +53,23 @@ def parse():
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--check-rows", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--traffic-calibration", action="store_true",
+                    help="only copy a 1 GiB device buffer 4 times (a kernel "
+                         "of known HBM traffic for scaling rocprofv3's "
+                         "FETCH_SIZE / WRITE_SIZE) and exit")
     return ap.parse_args()
+
+
+def traffic_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": n, "copies": 4}), flush=True)
 
 
 def projections_of(wl, D):
@@ -62,6 +78,9 @@ def projections_of(wl, D):
 
 def main():
     args = parse()
+    if args.traffic_calibration:
+        traffic_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(the projection shards by tokens with no exchange; see the "
@@ -272,14 +291,23 @@ def traffic_entry():
     summaries, valid only while the kernel source is unchanged."""
     import hashlib
     f = ROOT / "profiles" / "gemm_traffic.json"
-    src = ROOT / "w8a8_int8_gemm_amd" / "csrc" / "gemm.hip"
     if not f.exists():
         return None
     rec = json.loads(f.read_text())
-    sha = hashlib.sha256(src.read_bytes()).hexdigest()
-    if rec.get("kernel_sha256") != sha:
+    if rec.get("kernel_sha256") != kernel_source_sha256():
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("traffic")
+
+
+def kernel_source_sha256():
+    """Hash of the GEMM kernel's sources (the kernel file and the shared
+    device header); traffic figures are only valid for this exact code."""
+    import hashlib
+    csrc = ROOT / "w8a8_int8_gemm_amd" / "csrc"
+    h = hashlib.sha256()
+    for name in ("gemm.hip", "internal.h"):
+        h.update((csrc / name).read_bytes())
+    return h.hexdigest()
 
 
 def bf16_baseline(torch, D, BL, wl, x0, blk, dev, warmup, reps):

@@ -104,18 +104,6 @@ __device__ __forceinline__ v4i read_lds16(const int8_t *lds_base, int off) {
   return *reinterpret_cast<const v4i *>(lds_base + off);
 }
 
-typedef float f2v __attribute__((ext_vector_type(2)));
-typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
-
-// Two binary32 values -> two BF16 (round to nearest, ties to even) packed in
-// one dword, low half first: gfx950's v_cvt_pk_bf16_f32.  The epilogue's
-// values are finite or +-Inf (finite scales and activations are a
-// documented precondition), never NaN.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const bf2v b = __builtin_convertvector(f2v{lo, hi}, bf2v);
-  return __builtin_bit_cast(uint32_t, b);
-}
-
 // Block id -> (token tile, channel tile).
 __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n,
                                         int group_m, int &tm, int &tn) {

@@ -33,20 +33,51 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ uint32_t quant_pair(uint32_t packed_bf16, float s,
-                                               int shift_lo, int shift_hi) {
-  // Two BF16 -> two INT8 codes, placed at the given bit offsets.
-  float f0 = bf16_to_f32(packed_bf16 & 0xFFFFu);
-  float f1 = bf16_to_f32(packed_bf16 >> 16);
-  float r0 = fminf(fmaxf(rintf(f0 / s), -127.0f), 127.0f);
-  float r1 = fminf(fmaxf(rintf(f1 / s), -127.0f), 127.0f);
-  uint32_t q0 = (uint32_t)((int)r0) & 0xFFu;
-  uint32_t q1 = (uint32_t)((int)r1) & 0xFFu;
-  return (q0 << shift_lo) | (q1 << shift_hi);
+// Per-row constants of the quantizer.  For rows whose scale is a normal
+// number the codes come from u = fma(x, 1/s, 128): the reciprocal (one
+// IEEE division per row), the product and the sum together stay within
+// 2.3e-5 of 128 + RN(x/s) (|x/s| <= 127 + 2^-17), so when u is farther
+// than 2^-14 from a half-integer, rounding u to the nearest integer gives
+// exactly 128 + round_half_even(RN(x/s)).  The remaining elements (about
+// one in 8000) and rows with a subnormal scale use the division itself.
+struct QuantRow {
+  float s, r;
+  bool fast;
+};
+
+__device__ __forceinline__ QuantRow quant_row(float amax) {
+  QuantRow q;
+  q.s = amax / 127.0f;
+  q.fast = q.s >= 0x1p-126f;
+  q.r = q.fast ? 1.0f / q.s : 0.0f;
+  return q;
+}
+
+// Code of one value as the byte (q + 128), q = clamp(rint(x / s)).
+__device__ __noinline__ float quant_biased_exact(float x, float s) {
+  const float q = fminf(fmaxf(rintf(x / s), -127.0f), 127.0f);
+  return q + 128.0f;  // exact small integer
+}
+
+// Four BF16 values (two packed pairs) -> four INT8 codes in one dword.
+__device__ __forceinline__ uint32_t quant4(uint32_t p01, uint32_t p23,
+                                           const QuantRow &R) {
+  const float f[4] = {bf16_to_f32(p01 & 0xFFFFu), bf16_to_f32(p01 >> 16),
+                      bf16_to_f32(p23 & 0xFFFFu), bf16_to_f32(p23 >> 16)};
+  uint32_t out = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float u = R.fast ? fmaf(f[e], R.r, 128.0f) : 0.5f;
+    const float fr = __builtin_amdgcn_fractf(u);
+    if (!(fabsf(fr - 0.5f) > 0x1p-14f)) u = quant_biased_exact(f[e], R.s);
+    // round to the nearest integer in [0, 255] and insert as byte e
+    out = __builtin_amdgcn_cvt_pk_u8_f32(u, e, out);
+  }
+  return out ^ 0x80808080u;  // biased byte -> two's complement code
 }
 
 __device__ __forceinline__ uint32_t silu_pair(uint32_t packed) {
-  return silu_bf16_bits(packed & 0xFFFFu) | (silu_bf16_bits(packed >> 16) << 16);
+  return silu_bf16x2(packed);
 }
 
 __device__ __forceinline__ float absmax_pair(uint32_t packed) {
@@ -127,7 +158,8 @@ __global__ __launch_bounds__(kThreads) void row_kernel(
   }
 
   // Quantize: scale = amax / 127 (IEEE division), zero row -> scale 0.
-  const float s = amax / 127.0f;
+  const QuantRow R = quant_row(amax);
+  const float s = R.s;
   if (lane == 0 && part == 0) scale[row] = s;
   uint2 *qr = reinterpret_cast<uint2 *>(static_cast<int8_t *>(out) +
                                         row * (int64_t)K);
@@ -138,8 +170,8 @@ __global__ __launch_bounds__(kThreads) void row_kernel(
       uint2 o = make_uint2(0, 0);
       if (s != 0.0f) {
         const v4u c = v[i];
-        o.x = quant_pair(c.x, s, 0, 8) | quant_pair(c.y, s, 16, 24);
-        o.y = quant_pair(c.z, s, 0, 8) | quant_pair(c.w, s, 16, 24);
+        o.x = quant4(c.x, c.y, R);
+        o.y = quant4(c.z, c.w, R);
       }
       qr[j] = o;
     }
