@@ -230,6 +230,32 @@ def test_linear(orc, M, N, K):
     assert np.array_equal(y, orc.linear(x, w, sw, b))
 
 
+@pytest.mark.parametrize("M,N,K", [(4097, 4096, 1664), (4097, 4096, 1024)])
+def test_gemm_tail_split(orc, M, N, K):
+    # 17 x 16 tiles of 256 x 256: one full wave of 256 tiles, then the 16
+    # tiles of the one-row last token tile split K (26 stages in 3 slices of
+    # 8/9/9, or 16 stages in 2) and summed by the tail reduction.
+    ws = B.workspace_bytes(M, N, K)
+    say(f"gemm tail split M={M} N={N} K={K} workspace={ws}")
+    assert ws > 0
+    a, w, sa, sw, bias = gemm_inputs(M, N, K, 4)
+    args = (dev(a), dev(sa), dev(w), dev(sw), dev_bf16(bias))
+    ig = Guarded((M, N), torch.int32)
+    bg = Guarded((M, N), torch.bfloat16)
+    B.gemm(*args, out_dtype=torch.int32, out=ig.t)
+    B.gemm(*args, out_dtype=torch.bfloat16, out=bg.t)
+    torch.cuda.synchronize()
+    got = ig.t.cpu().numpy()
+    yb = host_bf16(bg.t)
+    ig.check()
+    bg.check()
+    want = orc.gemm_i32(a, w)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} accumulators differ: {bad[:5].tolist()}"
+    _, rb = orc.epilogue(want, sa, sw, bias)
+    assert np.array_equal(yb, rb)
+
+
 def test_gemm_deterministic():
     say("gemm determinism")
     M, N, K = 4096, 5376, 5376

@@ -33,6 +33,7 @@
 //     are exact in any order) and applies the epilogue.
 #include "internal.h"
 
+#include <algorithm>
 #include <type_traits>
 
 #pragma clang fp contract(off)
@@ -47,7 +48,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void gbl_void;
 
 constexpr int kXcds = 8;
-constexpr int EPI_PARTIAL = 3;  // split-K slice: raw INT32 to the workspace
+constexpr int EPI_PARTIAL = 3;       // split-K slice: raw INT32, [M,N] layout
+constexpr int EPI_PARTIAL_TILE = 4;  // tail split-K slice: raw INT32 per tile
 
 template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int GROUP_M_,
           int NS_>
@@ -104,14 +106,21 @@ __device__ __forceinline__ v4i read_lds16(const int8_t *lds_base, int off) {
   return *reinterpret_cast<const v4i *>(lds_base + off);
 }
 
-// Block id -> (token tile, channel tile).
-__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n,
-                                        int group_m, int &tm, int &tn) {
-  const int T = tiles_m * tiles_n;
+// The hardware deals workgroups round-robin to the 8 XCDs; remap block id
+// `bid` of a T-block grid so that each XCD owns a contiguous run of tile
+// indices.
+__device__ __forceinline__ int xcd_remap(int bid, int T) {
   const int xcd = bid % kXcds;
   const int local = bid / kXcds;
   const int per = T / kXcds, rem = T % kXcds;
-  const int L = xcd * per + min(xcd, rem) + local;
+  return xcd * per + min(xcd, rem) + local;
+}
+
+// Tile index -> (token tile, channel tile): groups of `group_m` token tiles
+// sweep all channel tiles, token tile fastest within a group, so tiles in
+// flight together share A rows and W rows.
+__device__ __forceinline__ void grouped_tile(int L, int tiles_m, int tiles_n,
+                                             int group_m, int &tm, int &tn) {
   const int span = group_m * tiles_n;
   const int g = L / span;
   const int first = g * group_m;
@@ -182,6 +191,9 @@ struct KernelArgs {
   int tiles_m, tiles_n;
   int stages_total;  // K / BK
   int splits;
+  int group_m;
+  int tile_base;     // first tile index of this launch
+  int remap;         // 1: XCD remap of block ids over the grid
 };
 
 template <class C, int EPI>
@@ -195,7 +207,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(KernelArgs p) {
   const int wave_n = wave % C::WGN;
 
   int tm, tn;
-  tile_of(blockIdx.x, p.tiles_m, p.tiles_n, C::GROUP_M, tm, tn);
+  const int L = p.remap ? xcd_remap(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  grouped_tile(p.tile_base + L, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
   const int m0 = tm * C::BM;
   const int n0 = tn * C::BN;
 
@@ -300,7 +313,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(KernelArgs p) {
   };
   // Interleave: after every MFMAS/READS MFMAs, one fragment read.
   auto interleave = [&]() {
-#ifndef W8A8_NO_INTERLEAVE_HINTS
+#ifndef W8A8_INTERLEAVE
+#define W8A8_INTERLEAVE 0
+#endif
+#if W8A8_INTERLEAVE == 0
 #pragma unroll
     for (int r = 0; r < READS; ++r) {
       __builtin_amdgcn_sched_group_barrier(0x008, MFMAS / READS, 0);
@@ -308,6 +324,20 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(KernelArgs p) {
     }
     if constexpr (MFMAS % READS != 0)
       __builtin_amdgcn_sched_group_barrier(0x008, MFMAS % READS, 0);
+#elif W8A8_INTERLEAVE == 1
+    __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, MFMAS, 0);
+#elif W8A8_INTERLEAVE == 2
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - 1, 0);
+#elif W8A8_INTERLEAVE == 3
+#pragma unroll
+    for (int r = 0; r < READS / 2; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - READS / 2, 0);
 #endif
   };
   // One stage: its KS k-steps; the last one crosses into stage kt+1.
@@ -422,6 +452,27 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(KernelArgs p) {
     }
     return;
   }
+  if constexpr (EPI == EPI_PARTIAL_TILE) {
+    // Raw accumulators of this K slice in a tile-local [BM][BN] block of the
+    // workspace: slice z of tail tile blockIdx.x.  Rows/columns past M or N
+    // hold values of clamped rows and are never read back.
+    int *dst = static_cast<int *>(p.out) +
+               ((int64_t)z * gridDim.x + blockIdx.x) * (C::BM * C::BN);
+#pragma unroll
+    for (int j = 0; j < C::TM; ++j) {
+      const int lm = wave_m * C::WM + j * 32 + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < C::TN; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int ln = wave_n * C::WN + i * 32 + 8 * g + 4 * (lane >> 5);
+          *reinterpret_cast<v4i *>(dst + lm * C::BN + ln) =
+              v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                  acc[i][j][4 * g + 3]};
+        }
+    }
+    return;
+  }
   const int64_t MN = (int64_t)p.M * p.N;
 #pragma unroll
   for (int j = 0; j < C::TM; ++j) {
@@ -514,6 +565,56 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
   }
 }
 
+// Sum of the K slices of the tail tiles + epilogue.  Block b covers tail
+// tile b / QB (QB blocks of 256 threads per tile, 4 outputs per thread).
+template <int BM, int BN, int EPI>
+__global__ __launch_bounds__(256) void tail_reduce_kernel(
+    const int *__restrict__ part, int splits, int ntail, int tile_base,
+    int tiles_m, int tiles_n, int group_m, const float *__restrict__ sa,
+    const float *__restrict__ sw, const uint16_t *__restrict__ bias,
+    void *__restrict__ out, int M, int N) {
+  constexpr int QB = BM * BN / 4 / 256;
+  const int t = blockIdx.x / QB;
+  const int q = (blockIdx.x % QB) * 256 + threadIdx.x;
+  const int lm = q / (BN / 4), ln = (q % (BN / 4)) * 4;
+  int tm, tn;
+  grouped_tile(tile_base + t, tiles_m, tiles_n, group_m, tm, tn);
+  const int m = tm * BM + lm, n = tn * BN + ln;
+  if (m >= M || n >= N) return;
+  const int64_t tile_elems = (int64_t)BM * BN;
+  const int *src = part + (int64_t)t * tile_elems + lm * BN + ln;
+  v4i s = *reinterpret_cast<const v4i *>(src);
+  for (int z = 1; z < splits; ++z)
+    s += *reinterpret_cast<const v4i *>(src + (int64_t)z * ntail * tile_elems);
+  const int64_t o = (int64_t)m * N + n;
+  if (EPI == EPI_I32) {
+    *reinterpret_cast<v4i *>(static_cast<int *>(out) + o) = s;
+    return;
+  }
+  const float sam = sa[m];
+  const float4 swn = *reinterpret_cast<const float4 *>(sw + n);
+  float t0 = ((float)s.x * sam) * swn.x;
+  float t1 = ((float)s.y * sam) * swn.y;
+  float t2 = ((float)s.z * sam) * swn.z;
+  float t3 = ((float)s.w * sam) * swn.w;
+  if (bias) {
+    const uint2 b = *reinterpret_cast<const uint2 *>(bias + n);
+    t0 = t0 + bf16_to_f32(b.x & 0xFFFFu);
+    t1 = t1 + bf16_to_f32(b.x >> 16);
+    t2 = t2 + bf16_to_f32(b.y & 0xFFFFu);
+    t3 = t3 + bf16_to_f32(b.y >> 16);
+  }
+  if (EPI == EPI_FP32) {
+    *reinterpret_cast<float4 *>(static_cast<float *>(out) + o) =
+        make_float4(t0, t1, t2, t3);
+  } else {
+    uint2 v;
+    v.x = pack_bf16x2(t0, t1);
+    v.y = pack_bf16x2(t2, t3);
+    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + o) = v;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Tile configurations
 // ---------------------------------------------------------------------------
@@ -531,8 +632,15 @@ using CfgSkinny = Cfg<W8A8_CFG_SKINNY>;
 template <class C>
 hipError_t set_lds_limit();
 
+template <class C, int EPI>
+void launch_main(const KernelArgs &p, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_kernel<C, EPI>), grid, dim3(C::THREADS), C::LDS,
+                     stream, p);
+}
+
 template <class C>
-hipError_t launch_cfg(const GemmArgs &g, int splits, hipStream_t stream) {
+hipError_t launch_cfg(const GemmArgs &g, const GemmPlan &plan,
+                      hipStream_t stream) {
   // Dynamic LDS above 64 KiB needs an explicit opt-in, once per process.
   static const hipError_t lds_ok = set_lds_limit<C>();
   if (lds_ok != hipSuccess) return lds_ok;
@@ -548,30 +656,50 @@ hipError_t launch_cfg(const GemmArgs &g, int splits, hipStream_t stream) {
   p.tiles_m = (int)((g.M + C::BM - 1) / C::BM);
   p.tiles_n = (int)((g.N + C::BN - 1) / C::BN);
   p.stages_total = (int)(g.K / C::BK);
-  p.splits = splits;
-  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n), 1, (unsigned)splits);
-  const dim3 block(C::THREADS);
-  if (splits == 1) {
+  p.splits = plan.splits;
+  p.group_m = plan.group_m;
+  p.tile_base = 0;
+  p.remap = 1;
+  const dim3 grid((unsigned)plan.main_tiles, 1, (unsigned)plan.splits);
+  if (plan.splits == 1) {
     p.out = g.out;
     switch (g.epi) {
-      case EPI_BF16:
-        hipLaunchKernelGGL((gemm_kernel<C, EPI_BF16>), grid, block, C::LDS,
-                           stream, p);
-        break;
-      case EPI_FP32:
-        hipLaunchKernelGGL((gemm_kernel<C, EPI_FP32>), grid, block, C::LDS,
-                           stream, p);
-        break;
-      default:
-        hipLaunchKernelGGL((gemm_kernel<C, EPI_I32>), grid, block, C::LDS,
-                           stream, p);
-        break;
+      case EPI_BF16: launch_main<C, EPI_BF16>(p, grid, stream); break;
+      case EPI_FP32: launch_main<C, EPI_FP32>(p, grid, stream); break;
+      default: launch_main<C, EPI_I32>(p, grid, stream); break;
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || plan.tail_splits <= 1) return e;
+    // Tail: the last tiles (less than one wave of the chip) split K so the
+    // chip stays busy; INT32 slices in the workspace, then a reduction.
+    KernelArgs t = p;
+    t.out = g.workspace;
+    t.splits = plan.tail_splits;
+    t.tile_base = plan.main_tiles;
+    t.remap = 0;
+    launch_main<C, EPI_PARTIAL_TILE>(
+        t, dim3((unsigned)plan.tail_tiles, 1, (unsigned)plan.tail_splits),
+        stream);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr int QB = C::BM * C::BN / 4 / 256;
+    const dim3 rgrid((unsigned)(plan.tail_tiles * QB));
+    const int *part = static_cast<const int *>(g.workspace);
+#define W8A8_TAIL(E)                                                          \
+  hipLaunchKernelGGL((tail_reduce_kernel<C::BM, C::BN, E>), rgrid, dim3(256), \
+                     0, stream, part, plan.tail_splits, plan.tail_tiles,     \
+                     plan.main_tiles, p.tiles_m, p.tiles_n, p.group_m, g.sa, \
+                     g.sw, g.bias, g.out, p.M, p.N)
+    switch (g.epi) {
+      case EPI_BF16: W8A8_TAIL(EPI_BF16); break;
+      case EPI_FP32: W8A8_TAIL(EPI_FP32); break;
+      default: W8A8_TAIL(EPI_I32); break;
+    }
+#undef W8A8_TAIL
     return hipGetLastError();
   }
   p.out = g.workspace;
-  hipLaunchKernelGGL((gemm_kernel<C, EPI_PARTIAL>), grid, block, C::LDS,
-                     stream, p);
+  launch_main<C, EPI_PARTIAL>(p, grid, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t quads = g.M * g.N / 4;
@@ -581,17 +709,17 @@ hipError_t launch_cfg(const GemmArgs &g, int splits, hipStream_t stream) {
   switch (g.epi) {
     case EPI_BF16:
       hipLaunchKernelGGL(splitk_reduce_kernel<EPI_BF16>, dim3((unsigned)blocks),
-                         dim3(256), 0, stream, part, splits, g.sa, g.sw,
+                         dim3(256), 0, stream, part, plan.splits, g.sa, g.sw,
                          g.bias, g.out, p.M, p.N);
       break;
     case EPI_FP32:
       hipLaunchKernelGGL(splitk_reduce_kernel<EPI_FP32>, dim3((unsigned)blocks),
-                         dim3(256), 0, stream, part, splits, g.sa, g.sw,
+                         dim3(256), 0, stream, part, plan.splits, g.sa, g.sw,
                          g.bias, g.out, p.M, p.N);
       break;
     default:
       hipLaunchKernelGGL(splitk_reduce_kernel<EPI_I32>, dim3((unsigned)blocks),
-                         dim3(256), 0, stream, part, splits, g.sa, g.sw,
+                         dim3(256), 0, stream, part, plan.splits, g.sa, g.sw,
                          g.bias, g.out, p.M, p.N);
       break;
   }
@@ -614,6 +742,9 @@ hipError_t set_lds_limit() {
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void *)gemm_kernel<C, EPI_PARTIAL>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void *)gemm_kernel<C, EPI_PARTIAL_TILE>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
   }
   return e;
 }
@@ -622,18 +753,51 @@ constexpr int kCfgLarge = 0;
 constexpr int kCfgSkinny = 1;
 constexpr int kCUs = 256;
 
+// Token tiles per group of the tile order: a narrow output (few channel
+// tiles) affords taller groups within one wave of work groups.
+#ifndef W8A8_GROUP_M_NARROW
+#define W8A8_GROUP_M_NARROW 4
+#endif
+#ifndef W8A8_GROUP_M_WIDE
+#define W8A8_GROUP_M_WIDE 4
+#endif
+// Fewest K slices that make a split tail launch worthwhile.
+#ifndef W8A8_TAIL_MIN_SPLITS
+#define W8A8_TAIL_MIN_SPLITS 2
+#endif
+
 }  // namespace
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
-  GemmPlan plan{kCfgLarge, 1, 0};
-  const int64_t large_tiles =
-      ((M + CfgLarge::BM - 1) / CfgLarge::BM) * ((N + CfgLarge::BN - 1) / CfgLarge::BN);
-  if (large_tiles >= kCUs) return plan;
+  GemmPlan plan{kCfgLarge, 1, CfgLarge::GROUP_M, 0, 0, 0, 0};
+  const int64_t tiles_n = (N + CfgLarge::BN - 1) / CfgLarge::BN;
+  plan.group_m = tiles_n <= 32 ? W8A8_GROUP_M_NARROW : W8A8_GROUP_M_WIDE;
+  const int64_t large_tiles = ((M + CfgLarge::BM - 1) / CfgLarge::BM) * tiles_n;
+  if (large_tiles >= kCUs) {
+    plan.main_tiles = (int)large_tiles;
+    // A last partial wave of tiles leaves most CUs idle for a whole tile
+    // time.  When it holds few tiles, run it as a second launch whose tiles
+    // split K so that about one wave of work groups shares it (each slice
+    // keeps at least 8 stages).
+    const int64_t rem = large_tiles % kCUs;
+    const int64_t stages = K / CfgLarge::BK;
+    const int64_t splits = std::min<int64_t>(rem ? kCUs / rem : 0, stages / 8);
+    if (rem > 0 && splits >= W8A8_TAIL_MIN_SPLITS) {
+      plan.main_tiles = (int)(large_tiles - rem);
+      plan.tail_tiles = (int)rem;
+      plan.tail_splits = (int)splits;
+      plan.workspace = (size_t)(rem * splits) * CfgLarge::BM * CfgLarge::BN *
+                       sizeof(int32_t);
+    }
+    return plan;
+  }
   // Few tiles: smaller tiles, and split K while the grid is under one wave
   // of the chip and each slice keeps at least 8 stages.
   plan.config = kCfgSkinny;
+  plan.group_m = CfgSkinny::GROUP_M;
   const int64_t tiles =
       ((M + CfgSkinny::BM - 1) / CfgSkinny::BM) * ((N + CfgSkinny::BN - 1) / CfgSkinny::BN);
+  plan.main_tiles = (int)tiles;
   const int64_t stages = K / CfgSkinny::BK;
   int splits = 1;
   while (tiles * splits * 2 <= kCUs && stages / (splits * 2) >= 8) splits *= 2;
@@ -644,8 +808,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_gemm(const GemmArgs &args, const GemmPlan &plan,
                        hipStream_t stream) {
-  if (plan.config == kCfgLarge) return launch_cfg<CfgLarge>(args, plan.splits, stream);
-  return launch_cfg<CfgSkinny>(args, plan.splits, stream);
+  if (plan.config == kCfgLarge) return launch_cfg<CfgLarge>(args, plan, stream);
+  return launch_cfg<CfgSkinny>(args, plan, stream);
 }
 
 }  // namespace w8a8

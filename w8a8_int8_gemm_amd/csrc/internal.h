@@ -122,9 +122,13 @@ struct GemmArgs {
 
 // Plan of one GEMM launch: which tile configuration, how many K splits.
 struct GemmPlan {
-  int config;      // index into the kernel table
-  int splits;      // 1 = no split-K
-  size_t workspace;  // bytes of INT32 partials (0 when splits == 1)
+  int config;        // index into the kernel table
+  int splits;        // split-K over the whole output (1 = none)
+  int group_m;       // token tiles per group in the tile order
+  int main_tiles;    // tiles of the main launch (all tiles unless a tail)
+  int tail_tiles;    // trailing tiles run split-K in a second launch
+  int tail_splits;   // K slices per tail tile (0 = no tail launch)
+  size_t workspace;  // bytes of INT32 partials needed (0 if none)
 };
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
