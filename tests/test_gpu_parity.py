@@ -123,18 +123,29 @@ def test_silu_all_bf16_values(orc):
     assert np.count_nonzero(d) == 0, f"{np.count_nonzero(d)} differ by 1 ulp"
 
 
-@pytest.mark.parametrize("M,K", [(4, 5376), (3, 21504), (17, 128)])
+# Row counts above the number of CUs make each work group of the fused
+# kernel walk several rows (with the next row prefetched); K = 90112 takes
+# the path without prefetch; K = 8 is a single chunk.
+@pytest.mark.parametrize("M,K", [(4, 5376), (3, 21504), (17, 128),
+                                 (600, 21504), (300, 5376), (5, 49152),
+                                 (2, 90112), (3, 8)])
 def test_quantize_act_silu(orc, M, K):
     say(f"quantize_act_silu M={M} K={K}")
     g = np.random.default_rng(M * K)
     x = D.to_bf16_bits((g.standard_normal((M, K)) * 30).astype(np.float32))
+    if M >= 6:
+        x[:6] = edge_rows(K)
     xd = dev_bf16(x)
-    q, s = B.quantize_act(xd, silu=True)
+    qg = Guarded((M, K), torch.int8)
+    sg = Guarded((M,), torch.float32)
+    q, s = B.quantize_act(xd, silu=True, out=(qg.t, sg.t))
     h = B.silu(xd)
     torch.cuda.synchronize()
     h_ref = orc.silu_bf16(x)
     assert np.array_equal(host_bf16(h), h_ref)
     q_ref, s_ref = orc.quantize_act(h_ref)
+    qg.check()
+    sg.check()
     assert np.array_equal(s.cpu().numpy().view(np.uint32),
                           s_ref.view(np.uint32))
     assert np.array_equal(q.cpu().numpy(), q_ref)

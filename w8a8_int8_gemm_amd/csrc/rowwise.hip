@@ -15,7 +15,20 @@
 // store instruction of a wave on 1 KiB (loads) or 512 B (INT8 stores) of
 // consecutive bytes.  The row maximum is a wave64 butterfly reduction
 // (and, for WPR = 4, one LDS exchange between the row's waves).
+//
+// SiLU kernels: a BF16 input has only 65536 bit patterns, so SiLU is a table
+// lookup.  The table (128 KiB) is built in device memory by a small kernel
+// that evaluates the correctly rounded SiLU of every pattern, enqueued on
+// the caller's stream ahead of each SiLU kernel (so it is always complete
+// when read; a concurrent rebuild on another stream writes the same bits).
+// The SiLU kernels keep one work group per CU, copy the table into LDS once
+// and then stream rows (or chunks) through it: two LDS reads and a few
+// integer operations per pair of values replace the exp / reciprocal
+// evaluation.
 #include "internal.h"
+
+#include <mutex>
+#include <unordered_map>
 
 namespace w8a8 {
 namespace {
@@ -25,7 +38,7 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;  // 4 waves of 64
 constexpr int kWaves = kThreads / 64;
 
-enum RowOp : int { OP_QUANT = 0, OP_QUANT_SILU = 1, OP_RENORM = 2 };
+enum RowOp : int { OP_QUANT = 0, OP_RENORM = 2 };
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -76,10 +89,6 @@ __device__ __forceinline__ uint32_t quant4(uint32_t p01, uint32_t p23,
   return out ^ 0x80808080u;  // biased byte -> two's complement code
 }
 
-__device__ __forceinline__ uint32_t silu_pair(uint32_t packed) {
-  return silu_bf16x2(packed);
-}
-
 __device__ __forceinline__ float absmax_pair(uint32_t packed) {
   return fmaxf(fabsf(bf16_to_f32(packed & 0xFFFFu)),
                fabsf(bf16_to_f32(packed >> 16)));
@@ -112,13 +121,7 @@ __global__ __launch_bounds__(kThreads) void row_kernel(
     const int j = (i * WPR + part) * 64 + lane;
     v[i] = v4u{0, 0, 0, 0};
     if (row_ok && j < chunks) {
-      v4u c = __builtin_nontemporal_load(xr + j);
-      if (OP == OP_QUANT_SILU) {
-        c.x = silu_pair(c.x);
-        c.y = silu_pair(c.y);
-        c.z = silu_pair(c.z);
-        c.w = silu_pair(c.w);
-      }
+      const v4u c = __builtin_nontemporal_load(xr + j);
       v[i] = c;
       amax = fmaxf(amax, fmaxf(fmaxf(absmax_pair(c.x), absmax_pair(c.y)),
                                fmaxf(absmax_pair(c.z), absmax_pair(c.w))));
@@ -178,19 +181,172 @@ __global__ __launch_bounds__(kThreads) void row_kernel(
   }
 }
 
-__global__ __launch_bounds__(kThreads) void silu_kernel(
+// ---------------------------------------------------------------------------
+// SiLU through a lookup table
+// ---------------------------------------------------------------------------
+
+constexpr int kLutEntries = 65536;
+constexpr int kLutThreads = 1024;  // 16 waves, one work group per CU
+constexpr int kLutWaves = kLutThreads / 64;
+
+// SiLU of BF16 bit pattern i in the low (i even) or high (i odd) half of
+// dword i / 2.
+__device__ uint32_t g_silu_lut[kLutEntries / 2];
+
+__global__ __launch_bounds__(256) void silu_lut_build_kernel() {
+  const uint32_t i = blockIdx.x * 256 + threadIdx.x;  // pair index
+  g_silu_lut[i] = silu_bf16x2((2 * i) | ((2 * i + 1) << 16));
+}
+
+// Copy the table into this work group's LDS.
+__device__ __forceinline__ void lut_to_lds(uint32_t *lut) {
+  const v4u *src = reinterpret_cast<const v4u *>(g_silu_lut);
+  v4u *dst = reinterpret_cast<v4u *>(lut);
+  for (int i = threadIdx.x; i < kLutEntries / 8; i += blockDim.x)
+    dst[i] = src[i];
+  __syncthreads();
+}
+
+__device__ __forceinline__ uint32_t silu_lut_pair(const uint16_t *lut,
+                                                  uint32_t p) {
+  return (uint32_t)lut[p & 0xFFFFu] | ((uint32_t)lut[p >> 16] << 16);
+}
+
+__device__ __forceinline__ v4u silu_lut_chunk(const uint16_t *lut, v4u c) {
+  return v4u{silu_lut_pair(lut, c.x), silu_lut_pair(lut, c.y),
+             silu_lut_pair(lut, c.z), silu_lut_pair(lut, c.w)};
+}
+
+// SiLU + per-token quantization.  The whole work group owns one row at a
+// time (chunk j of the row is held by thread j mod 1024, CH chunks per
+// thread) and, for rows of up to 6 chunks per thread (K <= 49152), loads
+// its next row while it quantizes the current one.
+template <int CH>
+__global__ __launch_bounds__(kLutThreads, 1) void silu_quant_lut_kernel(
+    const uint16_t *x, int8_t *q, float *__restrict__ scale, int64_t M,
+    int K) {
+  __shared__ uint32_t lut32[kLutEntries / 2];
+  __shared__ float part_max[2][kLutWaves];
+  lut_to_lds(lut32);
+  const uint16_t *lut = reinterpret_cast<const uint16_t *>(lut32);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int chunks = K >> 3;
+
+  auto load_row = [&](int64_t row, v4u *v) {
+    const v4u *xr = reinterpret_cast<const v4u *>(x + row * (int64_t)K);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int j = i * kLutThreads + threadIdx.x;
+      v[i] = v4u{0, 0, 0, 0};
+      if (row < M && j < chunks) v[i] = __builtin_nontemporal_load(xr + j);
+    }
+  };
+
+  constexpr bool kPrefetch = CH <= 6;  // two row buffers fit in registers
+  v4u cur[CH], nxt[kPrefetch ? CH : 1];
+  int64_t row = blockIdx.x;
+  if (kPrefetch) load_row(row, cur);
+  for (int it = 0; row < M; ++it, row += gridDim.x) {
+    if (kPrefetch)
+      load_row(row + gridDim.x, nxt);  // rows past M load nothing
+    else
+      load_row(row, cur);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const v4u c = silu_lut_chunk(lut, cur[i]);  // zero chunks map to zero
+      cur[i] = c;
+      amax = fmaxf(amax, fmaxf(fmaxf(absmax_pair(c.x), absmax_pair(c.y)),
+                               fmaxf(absmax_pair(c.z), absmax_pair(c.w))));
+    }
+    amax = wave_max(amax);
+    if (lane == 0) part_max[it & 1][wave] = amax;
+    __syncthreads();
+    amax = part_max[it & 1][0];
+#pragma unroll
+    for (int w = 1; w < kLutWaves; ++w) amax = fmaxf(amax, part_max[it & 1][w]);
+
+    const QuantRow R = quant_row(amax);
+    if (threadIdx.x == 0) scale[row] = R.s;
+    uint2 *qr = reinterpret_cast<uint2 *>(q + row * (int64_t)K);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int j = i * kLutThreads + threadIdx.x;
+      if (j < chunks) {
+        uint2 o = make_uint2(0, 0);
+        if (R.s != 0.0f) {
+          o.x = quant4(cur[i].x, cur[i].y, R);
+          o.y = quant4(cur[i].z, cur[i].w, R);
+        }
+        qr[j] = o;
+      }
+    }
+    if (kPrefetch) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) cur[i] = nxt[kPrefetch ? i : 0];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kLutThreads, 1) void silu_lut_kernel(
     const uint16_t *x, uint16_t *y, int64_t chunks) {
+  __shared__ uint32_t lut32[kLutEntries / 2];
+  lut_to_lds(lut32);
+  const uint16_t *lut = reinterpret_cast<const uint16_t *>(lut32);
   const v4u *xs = reinterpret_cast<const v4u *>(x);
   v4u *ys = reinterpret_cast<v4u *>(y);
-  for (int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x; j < chunks;
-       j += (int64_t)gridDim.x * kThreads) {
-    v4u c = __builtin_nontemporal_load(xs + j);
-    c.x = silu_pair(c.x);
-    c.y = silu_pair(c.y);
-    c.z = silu_pair(c.z);
-    c.w = silu_pair(c.w);
-    __builtin_nontemporal_store(c, ys + j);
+  for (int64_t j = (int64_t)blockIdx.x * kLutThreads + threadIdx.x;
+       j < chunks; j += (int64_t)gridDim.x * kLutThreads)
+    __builtin_nontemporal_store(
+        silu_lut_chunk(lut, __builtin_nontemporal_load(xs + j)), ys + j);
+}
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  static std::mutex mu;
+  static std::unordered_map<int, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+          hipSuccess || n <= 0)
+    n = 256;
+  cache[dev] = n;
+  return n;
+}
+
+hipError_t build_silu_lut(hipStream_t stream) {
+  hipLaunchKernelGGL(silu_lut_build_kernel, dim3(kLutEntries / 2 / 256),
+                     dim3(256), 0, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_quant(const uint16_t *x, int8_t *q, float *scale,
+                             int64_t M, int64_t K, hipStream_t stream) {
+  hipError_t e = build_silu_lut(stream);
+  if (e != hipSuccess) return e;
+  const int chunks = (int)(K / 8);
+  const int ch = (chunks + kLutThreads - 1) / kLutThreads;
+  const dim3 grid((unsigned)(M < cu_count() ? M : cu_count()));
+#define W8A8_LUT_CASE(C)                                                     \
+  if (ch <= C) {                                                             \
+    hipLaunchKernelGGL((silu_quant_lut_kernel<C>), grid, dim3(kLutThreads), \
+                       0, stream, x, q, scale, M, (int)K);                   \
+    return hipGetLastError();                                                \
   }
+  W8A8_LUT_CASE(1)
+  W8A8_LUT_CASE(2)
+  W8A8_LUT_CASE(3)
+  W8A8_LUT_CASE(4)
+  W8A8_LUT_CASE(6)
+  W8A8_LUT_CASE(8)
+  W8A8_LUT_CASE(11)
+#undef W8A8_LUT_CASE
+  return hipErrorInvalidValue;
 }
 
 // Chunk-per-lane counts that are instantiated, per waves-per-row.
@@ -239,8 +395,7 @@ hipError_t launch_row_op(const uint16_t *x, void *out, float *scale,
 hipError_t launch_quantize_act(const uint16_t *x, int8_t *q, float *sa,
                                int64_t M, int64_t K, bool fuse_silu,
                                hipStream_t stream) {
-  if (fuse_silu)
-    return launch_row_op<OP_QUANT_SILU>(x, q, sa, M, K, stream);
+  if (fuse_silu) return launch_silu_quant(x, q, sa, M, K, stream);
   return launch_row_op<OP_QUANT>(x, q, sa, M, K, stream);
 }
 
@@ -253,10 +408,12 @@ hipError_t launch_silu(const uint16_t *x, uint16_t *y, int64_t n,
                        hipStream_t stream) {
   const int64_t chunks = n / 8;
   if (chunks == 0) return hipSuccess;
-  int64_t blocks = (chunks + kThreads - 1) / kThreads;
-  if (blocks > 256 * 16) blocks = 256 * 16;  // grid-stride beyond 16 per CU
-  hipLaunchKernelGGL(silu_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
-                     stream, x, y, chunks);
+  hipError_t e = build_silu_lut(stream);
+  if (e != hipSuccess) return e;
+  int64_t blocks = (chunks + kLutThreads - 1) / kLutThreads;
+  if (blocks > cu_count()) blocks = cu_count();
+  hipLaunchKernelGGL(silu_lut_kernel, dim3((unsigned)blocks),
+                     dim3(kLutThreads), 0, stream, x, y, chunks);
   return hipGetLastError();
 }
 
