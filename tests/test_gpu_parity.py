@@ -87,8 +87,10 @@ def edge_rows(K: int) -> np.ndarray:
 # quantization, SiLU, renormalization
 # ---------------------------------------------------------------------------
 
+# The M = 5000 and M = 4500 cases span thousands of work groups.
 QUANT_SHAPES = [(1, 8), (3, 128), (65, 5376), (64, 5632), (5, 5640),
-                (7, 21504), (2, 90112), (257, 384), (33, 1000)]
+                (7, 21504), (2, 90112), (257, 384), (33, 1000),
+                (5000, 5376), (4500, 1000)]
 
 
 @pytest.mark.parametrize("M,K", QUANT_SHAPES)
@@ -151,7 +153,7 @@ def test_quantize_act_silu(orc, M, K):
     assert np.array_equal(q.cpu().numpy(), q_ref)
 
 
-@pytest.mark.parametrize("M,K", [(6, 5376), (9, 21504), (5, 8)])
+@pytest.mark.parametrize("M,K", [(6, 5376), (9, 21504), (5, 8), (4200, 5376)])
 def test_pow2_renorm(orc, M, K):
     say(f"pow2_renorm M={M} K={K}")
     x = D.activations(M, K, seed=7)

@@ -453,24 +453,24 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(KernelArgs p) {
     return;
   }
   if constexpr (EPI == EPI_PARTIAL_TILE) {
-    // Raw accumulators of this K slice in a tile-local [BM][BN] block of the
-    // workspace: slice z of tail tile blockIdx.x.  Rows/columns past M or N
-    // hold values of clamped rows and are never read back.
+    // Raw accumulators of this K slice in a tile-local block of the
+    // workspace (slice z of tail tile blockIdx.x), in register order: the
+    // 4-register group g of accumulator (i, j) of wave w is one 1 KiB run,
+    // lane-major, so every store writes whole contiguous lines.  Rows and
+    // columns past M or N hold values of clamped rows; the reduction skips
+    // them.
     int *dst = static_cast<int *>(p.out) +
-               ((int64_t)z * gridDim.x + blockIdx.x) * (C::BM * C::BN);
+               ((int64_t)z * gridDim.x + blockIdx.x) * (C::BM * C::BN) +
+               wave * (C::TN * C::TM * 4 * 256) + lane * 4;
 #pragma unroll
-    for (int j = 0; j < C::TM; ++j) {
-      const int lm = wave_m * C::WM + j * 32 + (lane & 31);
+    for (int i = 0; i < C::TN; ++i)
 #pragma unroll
-      for (int i = 0; i < C::TN; ++i)
+      for (int j = 0; j < C::TM; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int ln = wave_n * C::WN + i * 32 + 8 * g + 4 * (lane >> 5);
-          *reinterpret_cast<v4i *>(dst + lm * C::BN + ln) =
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<v4i *>(dst + ((i * C::TM + j) * 4 + g) * 256) =
               v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                   acc[i][j][4 * g + 3]};
-        }
-    }
     return;
   }
   const int64_t MN = (int64_t)p.M * p.N;
@@ -566,23 +566,29 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
 }
 
 // Sum of the K slices of the tail tiles + epilogue.  Block b covers tail
-// tile b / QB (QB blocks of 256 threads per tile, 4 outputs per thread).
-template <int BM, int BN, int EPI>
+// tile b / QB (QB blocks of 256 threads per tile); thread q of the tile
+// reads the q-th 16-byte run of each slice (the partial-tile layout above)
+// and maps it back to its token row and 4 channels.
+template <class C, int EPI>
 __global__ __launch_bounds__(256) void tail_reduce_kernel(
     const int *__restrict__ part, int splits, int ntail, int tile_base,
     int tiles_m, int tiles_n, int group_m, const float *__restrict__ sa,
     const float *__restrict__ sw, const uint16_t *__restrict__ bias,
     void *__restrict__ out, int M, int N) {
-  constexpr int QB = BM * BN / 4 / 256;
+  constexpr int QB = C::BM * C::BN / 4 / 256;
   const int t = blockIdx.x / QB;
   const int q = (blockIdx.x % QB) * 256 + threadIdx.x;
-  const int lm = q / (BN / 4), ln = (q % (BN / 4)) * 4;
+  const int lane = q % 64, g = (q / 64) % 4, j = (q / 256) % C::TM;
+  const int i = (q / (256 * C::TM)) % C::TN;
+  const int wave = q / (256 * C::TM * C::TN);
+  const int lm = (wave / C::WGN) * C::WM + j * 32 + (lane & 31);
+  const int ln = (wave % C::WGN) * C::WN + i * 32 + 8 * g + 4 * (lane >> 5);
   int tm, tn;
   grouped_tile(tile_base + t, tiles_m, tiles_n, group_m, tm, tn);
-  const int m = tm * BM + lm, n = tn * BN + ln;
+  const int m = tm * C::BM + lm, n = tn * C::BN + ln;
   if (m >= M || n >= N) return;
-  const int64_t tile_elems = (int64_t)BM * BN;
-  const int *src = part + (int64_t)t * tile_elems + lm * BN + ln;
+  const int64_t tile_elems = (int64_t)C::BM * C::BN;
+  const int *src = part + (int64_t)t * tile_elems + q * 4;
   v4i s = *reinterpret_cast<const v4i *>(src);
   for (int z = 1; z < splits; ++z)
     s += *reinterpret_cast<const v4i *>(src + (int64_t)z * ntail * tile_elems);
@@ -686,7 +692,7 @@ hipError_t launch_cfg(const GemmArgs &g, const GemmPlan &plan,
     const dim3 rgrid((unsigned)(plan.tail_tiles * QB));
     const int *part = static_cast<const int *>(g.workspace);
 #define W8A8_TAIL(E)                                                          \
-  hipLaunchKernelGGL((tail_reduce_kernel<C::BM, C::BN, E>), rgrid, dim3(256), \
+  hipLaunchKernelGGL((tail_reduce_kernel<C, E>), rgrid, dim3(256),           \
                      0, stream, part, plan.tail_splits, plan.tail_tiles,     \
                      plan.main_tiles, p.tiles_m, p.tiles_n, p.group_m, g.sa, \
                      g.sw, g.bias, g.out, p.M, p.N)
