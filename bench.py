@@ -10,9 +10,11 @@ input, all of it in the library's HIP kernels on one stream:
 Inputs and weights are resident in HBM before timing starts.  Reported:
   value      = sum of 2*M*N*K over the step's GEMMs / step time (TOPS),
                quantization and glue time included;
-  roofline   = the INT8 GEMM kernel alone: its algorithmic ops / its
-               average launch time (HIP events around every launch), against
-               the dense INT8 MFMA peak of 5.0 POP/s;
+  roofline   = the INT8 GEMM alone (one w8a8_gemm call: the main kernel
+               launch and, where the last wave of tiles is short, its split-K
+               tail launch and reduction): algorithmic ops / average call
+               time (HIP events around every call, on the launch stream),
+               against the dense INT8 MFMA peak of 5.0 POP/s;
   cpu_baseline = the CPU oracle timed on a bounded row sample;
   bf16_baseline (context) = torch's BF16 linear (hipBLASLt) on the same
                shapes.
@@ -269,7 +271,9 @@ def main():
         },
         "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
         "roofline": {
-            "kernel": "gemm_kernel (INT8 MFMA + fused epilogue)",
+            "kernel": ("w8a8_gemm call: gemm_kernel (INT8 MFMA + fused "
+                       "epilogue), plus its split-K tail launch and tail "
+                       "reduction where the last wave of tiles is short"),
             "bound": "mfma",
             "achieved": round(gemm_tops, 2) if gemm_tops else None,
             "peak": INT8_PEAK_TOPS,
