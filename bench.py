@@ -19,6 +19,7 @@ Inputs and weights are resident in HBM before timing starts.  Reported:
   bf16_baseline (context) = torch's BF16 linear (hipBLASLt) on the same
                shapes.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 0-4]
+       [--fused-qkv]
 """
 from __future__ import annotations
 
@@ -55,6 +56,9 @@ def parse():
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--check-rows", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--fused-qkv", action="store_true",
+                    help="run Q, K and V as one GEMM over the concatenated "
+                         "weights [3N, K] (same outputs, bit for bit)")
     ap.add_argument("--traffic-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 4 times (a kernel "
                          "of known HBM traffic for scaling rocprofv3's "
@@ -121,8 +125,11 @@ def main():
     blocks = []
     for b in range(wl.blocks):
         params = D.block_params(wl, b, threads=threads)
-        blocks.append({p.name: BL.upload_proj(p, params[p.name], dev)
-                       for p in wl.projs})
+        dblk = {p.name: BL.upload_proj(p, params[p.name], dev)
+                for p in wl.projs}
+        if args.fused_qkv and not single:
+            dblk = BL.fuse_qkv(dblk)
+        blocks.append(dblk)
         if rows is not None:
             if single:
                 p = wl.projs[0]
@@ -146,7 +153,8 @@ def main():
 
     x0 = BL.to_device_bf16(x0_host, dev)
     xbuf = [torch.empty_like(x0), torch.empty_like(x0)]
-    runner = BL.BlockRunner(M, dev) if not single else None
+    runner = (BL.BlockRunner(M, dev, fused_qkv=args.fused_qkv)
+              if not single else None)
     if single:
         p0 = wl.projs[0]
         qbuf = torch.empty((M, p0.K), dtype=torch.int8, device=dev)
@@ -262,7 +270,8 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {
-            "workload": wl.name,
+            "workload": wl.name + ("+fused_qkv" if args.fused_qkv and
+                                   not single else ""),
             "tokens": M,
             "blocks": wl.blocks,
             "linears": wl.blocks * len(wl.projs),
@@ -327,8 +336,9 @@ def bf16_baseline(torch, D, BL, wl, x0, blk, dev, warmup, reps):
         if len(blk) == 1:
             n = next(iter(blk))
             return F.linear(x0, ws[n], bs[n])
-        for n in ("q", "k", "v", "o"):
-            F.linear(x0, ws[n], bs[n])
+        for n in blk:
+            if n not in ("fc1", "fc2"):
+                F.linear(x0, ws[n], bs[n])
         h = F.linear(x0, ws["fc1"], bs["fc1"])
         return F.linear(F.silu(h), ws["fc2"], bs["fc2"])
 

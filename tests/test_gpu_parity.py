@@ -269,6 +269,36 @@ def test_gemm_tail_split(orc, M, N, K):
     assert np.array_equal(yb, rb)
 
 
+@pytest.mark.parametrize("M", [300, 4096])
+def test_fused_qkv_equals_separate(orc, M):
+    # one GEMM over [3N, K] (N = 16128 at the block's width) against the three
+    # separate projections: column blocks must match bit for bit
+    say(f"fused QKV M={M}")
+    H = D.HIDDEN
+    wl = D.WORKLOADS[1]
+    qkv = [p for p in wl.projs if p.name in ("q", "k", "v")]
+    params = {p.name: D.proj_params(p, wl.seed, 0) for p in qkv}
+    projs = {p.name: BL.upload_proj(p, params[p.name]) for p in qkv}
+    fused = BL.fuse_qkv(dict(projs))["qkv"]
+    assert fused.N == 3 * H and B.workspace_bytes(M, 3 * H, H) >= 0
+    x = D.activations(M, H, seed=11)
+    q, s = B.quantize_act(dev_bf16(x))
+    sep = [B.gemm(q, s, projs[n].w, projs[n].sw, projs[n].bias)
+           for n in ("q", "k", "v")]
+    yg = Guarded((M, 3 * H), torch.bfloat16)
+    B.gemm(q, s, fused.w, fused.sw, fused.bias, out=yg.t)
+    torch.cuda.synchronize()
+    y = host_bf16(yg.t)
+    yg.check()
+    for i, t in enumerate(sep):
+        assert np.array_equal(y[:, i * H:(i + 1) * H], host_bf16(t))
+    rows = D.row_sample(M, 6, 11)
+    for i, n in enumerate(("q", "k", "v")):
+        pp = params[n]
+        ref = orc.linear(x[rows], pp.w, pp.sw, pp.bias)
+        assert np.array_equal(y[rows, i * H:(i + 1) * H], ref)
+
+
 def test_gemm_deterministic():
     say("gemm determinism")
     M, N, K = 4096, 5376, 5376

@@ -11,6 +11,12 @@ not part of the projection path, so the synthetic block feeds its input X
 to O and FC1 as well; that keeps four quantizations per block, as in the
 model.  Everything here is a sequence of library calls on one stream;
 outputs and scratch are preallocated once per token count.
+
+Fused QKV (optional): the Q, K and V weights concatenated along the output
+channels, [3N, K] with their scales and biases, run as one GEMM on the
+shared quantized input.  Every output column depends only on its own weight
+row, so the three column blocks of the fused output equal the separate
+outputs bit for bit; the larger N fills the chip in fewer, fuller waves.
 """
 from __future__ import annotations
 
@@ -51,12 +57,26 @@ def upload_proj(p: D.Proj, pp: D.ProjParams, device="cuda") -> DeviceProj:
                       to_device_bf16(pp.bias, device))
 
 
+def fuse_qkv(projs: dict) -> dict:
+    """Replace projs' q, k, v by one "qkv" projection [3N, K] (device
+    tensors concatenated along the output channels)."""
+    import torch
+    q, k, v = projs["q"], projs["k"], projs["v"]
+    assert q.K == k.K == v.K
+    fused = DeviceProj("qkv", q.N + k.N + v.N, q.K,
+                       torch.cat([q.w, k.w, v.w]), torch.cat([q.sw, k.sw, v.sw]),
+                       torch.cat([q.bias, k.bias, v.bias]))
+    out = {n: p for n, p in projs.items() if n not in ("q", "k", "v")}
+    out["qkv"] = fused
+    return out
+
+
 class BlockRunner:
     """Preallocated buffers for one token count M; ``run`` enqueues the
     block's kernels on the current stream (or ``stream``).  ``on_gemm`` is
     called around every GEMM launch (for per-kernel event timing)."""
 
-    def __init__(self, M: int, device="cuda"):
+    def __init__(self, M: int, device="cuda", fused_qkv: bool = False):
         import torch
         self.M = M
         H, F = D.HIDDEN, D.FFN
@@ -65,11 +85,17 @@ class BlockRunner:
         self.xs = [e(M, dt=torch.float32) for _ in range(3)]
         self.hq = e(M, F, dt=torch.int8)
         self.hs = e(M, dt=torch.float32)
-        self.out = {n: e(M, H, dt=torch.bfloat16) for n in ("q", "k", "v", "o",
-                                                            "fc2")}
+        self.out = {n: e(M, H, dt=torch.bfloat16) for n in ("o", "fc2")}
+        if fused_qkv:
+            self.out["qkv"] = e(M, 3 * H, dt=torch.bfloat16)
+            for i, n in enumerate(("q", "k", "v")):
+                self.out[n] = self.out["qkv"][:, i * H:(i + 1) * H]
+        else:
+            for n in ("q", "k", "v"):
+                self.out[n] = e(M, H, dt=torch.bfloat16)
         self.out["fc1"] = e(M, F, dt=torch.bfloat16)
         ws = max(B.workspace_bytes(M, H, H), B.workspace_bytes(M, F, H),
-                 B.workspace_bytes(M, H, F))
+                 B.workspace_bytes(M, H, F), B.workspace_bytes(M, 3 * H, H))
         self.ws = e(max(ws, 256), dt=torch.uint8)
 
     def run(self, x, projs: dict, stream=None, on_gemm=None):
@@ -83,9 +109,10 @@ class BlockRunner:
             if on_gemm:
                 on_gemm(name, "end")
 
-        # Q, K, V: one shared quantization of the block input.
+        # Q, K, V: one shared quantization of the block input (and, fused,
+        # one GEMM over the concatenated weights).
         B.quantize_act(x, out=(self.xq[0], self.xs[0]), stream=stream)
-        for n in ("q", "k", "v"):
+        for n in (("qkv",) if "qkv" in projs else ("q", "k", "v")):
             gemm(n, self.xq[0], self.xs[0])
         # attention output projection and FC1 quantize their own inputs.
         B.quantize_act(x, out=(self.xq[1], self.xs[1]), stream=stream)
