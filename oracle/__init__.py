@@ -60,10 +60,13 @@ class Oracle:
         P, I64 = ctypes.c_void_p, ctypes.c_int64
         sigs = {
             "orc_quantize_act": [P, I64, I64, P, P],
+            "orc_quantize_weight": [P, I64, I64, P, P],
+            "orc_check_scales": [P, I64, P],
             "orc_gemm_i32": [P, P, I64, I64, I64, P],
             "orc_epilogue": [P, P, P, P, I64, I64, P, P],
             "orc_linear": [P, P, P, P, I64, I64, I64, P],
             "orc_silu_bf16": [P, I64, P],
+            "orc_swiglu_bf16": [P, I64, I64, P],
             "orc_pow2_renorm": [P, I64, I64, P],
             "orc_num_threads": [],
         }
@@ -97,6 +100,24 @@ class Oracle:
         self._check(self.lib.orc_quantize_act(_ptr(x), M, K, _ptr(q),
                                               _ptr(sa)), "quantize_act")
         return q, sa
+
+    def quantize_weight(self, w_bf16: np.ndarray):
+        """w: uint16 [N,K] BF16 bits -> (q int8 [N,K], sw float32 [N])."""
+        w = _c(w_bf16, np.uint16)
+        N, K = w.shape
+        q = np.empty((N, K), np.int8)
+        sw = np.empty(N, np.float32)
+        self._check(self.lib.orc_quantize_weight(_ptr(w), N, K, _ptr(q),
+                                                 _ptr(sw)), "quantize_weight")
+        return q, sw
+
+    def check_scales(self, sw: np.ndarray) -> int:
+        """Number of scales that are not finite and > 0."""
+        sw = _c(sw, np.float32)
+        bad = np.zeros(1, np.int64)
+        self._check(self.lib.orc_check_scales(_ptr(sw), sw.size, _ptr(bad)),
+                    "check_scales")
+        return int(bad[0])
 
     def gemm_i32(self, a: np.ndarray, w: np.ndarray) -> np.ndarray:
         """a int8 [M,K], w int8 [N,K] -> acc int32 [M,N]."""
@@ -152,6 +173,17 @@ class Oracle:
                     "silu_bf16")
         return y
 
+    def swiglu_bf16(self, h_bf16) -> np.ndarray:
+        """h uint16 [M, 2F] (gate | up) -> y uint16 [M, F]."""
+        h = _c(h_bf16, np.uint16)
+        M, F2 = h.shape
+        if F2 % 2:
+            raise ValueError("odd width")
+        y = np.empty((M, F2 // 2), np.uint16)
+        self._check(self.lib.orc_swiglu_bf16(_ptr(h), M, F2 // 2, _ptr(y)),
+                    "swiglu_bf16")
+        return y
+
     def pow2_renorm(self, x_bf16) -> np.ndarray:
         x = _c(x_bf16, np.uint16)
         M, K = x.shape
@@ -189,6 +221,18 @@ def default() -> Oracle:
 
 def quantize_act(x_bf16):
     return default().quantize_act(x_bf16)
+
+
+def quantize_weight(w_bf16):
+    return default().quantize_weight(w_bf16)
+
+
+def check_scales(sw):
+    return default().check_scales(sw)
+
+
+def swiglu_bf16(h_bf16):
+    return default().swiglu_bf16(h_bf16)
 
 
 def gemm_i32(a, w):

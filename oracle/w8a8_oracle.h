@@ -55,6 +55,15 @@ uint16_t orc_f64_to_bf16(double d);
 int orc_quantize_act(const uint16_t *x, int64_t M, int64_t K,
                      int8_t *q, float *sa);
 
+/* Per-output-channel weight quantization: each row of w (BF16 [N,K], one
+ * row per output channel) is quantized like an activation row; an all-zero
+ * row gets codes 0 and scale 1 (scales must be finite and positive). */
+int orc_quantize_weight(const uint16_t *w, int64_t N, int64_t K,
+                        int8_t *q, float *sw);
+
+/* *bad = number of scales that are not finite and > 0. */
+int orc_check_scales(const float *sw, int64_t N, int64_t *bad);
+
 /* acc[m,n] = sum_k a[m,k] * w[n,k], exact, stored as INT32.
  * a: INT8 [M,K]; w: INT8 [N,K] (a Linear's stored layout). */
 int orc_gemm_i32(const int8_t *a, const int8_t *w, int64_t M, int64_t N,
@@ -76,6 +85,12 @@ int orc_linear(const uint16_t *x, const int8_t *w, const float *sw,
 /* Harness glue between FC1 and FC2: y = x / (1 + exp(-x)) evaluated in
  * binary64 and rounded once to BF16.  n elements. */
 int orc_silu_bf16(const uint16_t *x, int64_t n, uint16_t *y);
+
+/* Gated MLP glue (fused gate/up projection, width 2F per token): the
+ * first F values of a row are the gate g, the next F the up value u;
+ * y = BF16(BF16(silu(g)) * u): SiLU rounded once to BF16 as above, then
+ * the product rounded once to BF16.  h: BF16 [M, 2F]; y: BF16 [M, F]. */
+int orc_swiglu_bf16(const uint16_t *h, int64_t M, int64_t F, uint16_t *y);
 
 /* Harness glue between blocks: each row is scaled by 2^-e with
  * e = floor(log2(max_k |x[m,k]|)) so that its largest magnitude lies in

@@ -353,6 +353,67 @@ def check_linear_hand_worked(orc):
 
 
 # --------------------------------------------------------------------------
+# weight quantization (converter side) and the scale contract
+# --------------------------------------------------------------------------
+
+def _bits_of(tokens):
+    vals = [ex.from_hex_or_rational(t) for t in tokens]
+    bits = bf16_bits_exact(vals)
+    for i, t in enumerate(tokens):
+        if t.startswith("-") and vals[i] == 0:
+            bits[i] = 0x8000
+    return vals, bits
+
+
+def check_weight_quant_hand_worked(orc):
+    rows = _parse_table("weight_quant_hand_worked.txt")
+    assert len(rows) >= 5
+    width = max(len(r[1].split()) for r in rows)
+    for name, ws, scale, codes in rows:
+        vals, bits = _bits_of(ws.split())
+        # pad every row to one width with zeros (do not change amax)
+        w = np.zeros((2, width), np.uint16)
+        w[0, : len(bits)] = bits
+        q, sw = orc.quantize_weight(w)
+        want_s = ex.rn_f32(ex.from_hex_or_rational(scale))
+        assert Fraction(float(sw[0])) == want_s, f"{name}: scale {sw[0]}"
+        assert q[0, : len(bits)].tolist() == [int(c) for c in codes.split()]
+        assert not q[0, len(bits):].any()
+        # the all-zero second row: codes 0, scale exactly 1
+        assert float(sw[1]) == 1.0 and not q[1].any()
+
+
+def check_weight_quant_rows(orc):
+    # random rows: every code from exact rational arithmetic, every scale
+    # finite and positive
+    w = random_rows(21, 7, 96)
+    w[3] = 0
+    q, sw = orc.quantize_weight(w)
+    assert np.all(np.isfinite(sw)) and np.all(sw > 0)
+    for n in range(w.shape[0]):
+        vals = [Fraction(float(v)) for v in
+                (w[n].astype(np.uint32) << 16).view(np.float32)]
+        amax = max(abs(v) for v in vals)
+        if amax == 0:
+            assert float(sw[n]) == 1.0 and not q[n].any()
+            continue
+        s = ex.rn_f32(amax / 127)
+        assert Fraction(float(sw[n])) == s
+        want = [max(-127, min(127, ex.round_half_even_int(ex.rn_f32(v / s))))
+                for v in vals]
+        assert q[n].tolist() == want
+
+
+def check_scale_contract(orc):
+    sw = np.array([1.0, 0.0, -0.0, -1.0, np.inf, -np.inf, np.nan, 1e-45,
+                   3.4e38, 2.5e-3], np.float32)
+    # bad: 0, -0, -1, +inf, -inf, nan  (a positive subnormal is fine)
+    assert orc.check_scales(sw) == 6
+    assert orc.check_scales(np.ones(5, np.float32)) == 0
+    assert orc.check_scales(np.zeros(0, np.float32)) == 0
+
+
+# --------------------------------------------------------------------------
 # harness glue
 # --------------------------------------------------------------------------
 
@@ -400,6 +461,37 @@ def check_pow2_renorm(orc):
             assert Fraction(float(b)) == want
 
 
+def check_swiglu_hand_worked(orc):
+    rows = _parse_table("swiglu_hand_worked.txt")
+    assert len(rows) >= 5
+    for name, gs, us, ys in rows:
+        _, g = _bits_of(gs.split())
+        _, u = _bits_of(us.split())
+        yv, want = _bits_of(ys.split())
+        h = np.concatenate([g, u]).reshape(1, -1)
+        y = orc.swiglu_bf16(h)
+        assert y[0].tolist() == want.tolist(), f"{name}: {y[0]} != {want}"
+
+
+def check_swiglu_composition(orc):
+    # y = BF16(BF16(silu(g)) * u) with the gate first: the SiLU values come
+    # from the oracle's SiLU (pinned by check_silu), the product and its
+    # rounding from exact rational arithmetic
+    g = np.random.default_rng([31, 5])
+    M, F = 3, 200
+    gate = torch_bf16_bits((g.standard_normal((M, F)) * 4).astype(np.float32))
+    up = torch_bf16_bits((g.standard_normal((M, F)) * 3).astype(np.float32))
+    h = np.concatenate([gate, up], axis=1)
+    y = orc.swiglu_bf16(h)
+    s = orc.silu_bf16(gate)
+    sv = (s.astype(np.uint32) << 16).view(np.float32)
+    uv = (up.astype(np.uint32) << 16).view(np.float32)
+    yv = (y.astype(np.uint32) << 16).view(np.float32)
+    for a, b, c in zip(sv.ravel(), uv.ravel(), yv.ravel()):
+        want = ex.rn_bf16(Fraction(float(a)) * Fraction(float(b)))
+        assert Fraction(float(c)) == want
+
+
 ALL_CHECKS = [
     check_quant_hand_worked,
     check_quant_invariants,
@@ -413,4 +505,9 @@ ALL_CHECKS = [
     check_linear_hand_worked,
     check_silu,
     check_pow2_renorm,
+    check_weight_quant_hand_worked,
+    check_weight_quant_rows,
+    check_scale_contract,
+    check_swiglu_hand_worked,
+    check_swiglu_composition,
 ]

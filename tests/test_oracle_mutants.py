@@ -43,6 +43,19 @@ MUTANTS = {
     "bf16_f64_no_subnormal_floor": ("if (e < -126) e = -126;", ""),
     "silu_sign": ("v / (1.0 + exp(-v))", "v / (1.0 + exp(v))"),
     "pow2_off_by_one": ("int e = ex - 1;", "int e = ex;"),
+    "weight_zero_row_scale_zero": ("      sw[n] = 1.0f;", "      sw[n] = 0.0f;"),
+    "scales_zero_allowed": (
+        "if (!(isfinite(sw[n]) && sw[n] > 0.0f)) ++count;",
+        "if (!(isfinite(sw[n]) && sw[n] >= 0.0f)) ++count;"),
+    "scales_nan_allowed": (
+        "if (!(isfinite(sw[n]) && sw[n] > 0.0f)) ++count;",
+        "if (isinf(sw[n]) || sw[n] <= 0.0f) ++count;"),
+    "swiglu_halves_swapped": (
+        "const uint16_t *up = gate + F;",
+        "const uint16_t *up = gate; gate = gate + F;"),
+    "swiglu_unrounded_silu": (
+        "double s = (double)orc_bf16_to_f32(orc_f64_to_bf16(g / (1.0 + exp(-g))));",
+        "double s = g / (1.0 + exp(-g));"),
 }
 
 
