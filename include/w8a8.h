@@ -126,6 +126,31 @@ int w8a8_linear(const uint16_t *x, const int8_t *w_q, const float *w_scale,
                 int64_t K, void *workspace, size_t workspace_bytes,
                 void *stream);
 
+/*
+ * Per-output-channel weight quantization (the converter side of the
+ * GEMM: "feat(mps): support MiniMax-H3 INT8 inference on Apple M5",
+ * LightX2V pull request #1672, "Validation" and "Changes": weights become
+ * INT8 one row per output channel with a finite, positive FP32 scale).
+ *   w        BF16 [N,K] in a Linear's layout, 16-byte aligned.
+ *   w_q      INT8 [N,K] out, 8-byte aligned.
+ *   w_scale  FP32 [N] out, 4-byte aligned.
+ * Each row is quantized exactly as w8a8_quantize_act quantizes a token
+ * row, except that an all-zero row takes the scale 1 (its codes are 0), so
+ * every scale is finite and positive.  Shape, alignment and errors as
+ * w8a8_quantize_act with M = N.
+ */
+int w8a8_quantize_weight(const uint16_t *w, int64_t N, int64_t K,
+                         int8_t *w_q, float *w_scale, void *stream);
+
+/*
+ * Scale contract check: *bad_count (a device int32, 4-byte aligned)
+ * receives the number of entries of w_scale [N] that are not finite and
+ * > 0 (NaN, +-Inf, zero or negative), for weights produced elsewhere.
+ * 0 <= N < 2^31.  Errors: NULL, SHAPE, ALIGN, DEVICE, HIP.
+ */
+int w8a8_check_scales(const float *w_scale, int64_t N, int32_t *bad_count,
+                      void *stream);
+
 /* Workspace bytes w8a8_gemm needs for this shape (0 when none); 0 as well
  * for shapes the contract rejects. */
 size_t w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
@@ -145,10 +170,13 @@ int w8a8_last_hip_error(void);
  * Glue between projections (not part of the W8A8 method; it produces the
  * inputs a DiT block feeds to FC2 and to the next block).
  *
- * w8a8_silu_bf16: y[i] = x / (1 + exp(-x)) correctly rounded to BF16
- *   (evaluated in FP32, with FP64 for the rare elements whose FP32 value
- *   lies too close to a BF16 rounding midpoint to decide), for n elements; x and y 16-byte aligned, n >= 0 and n % 8 == 0; x and y
- *   may be the same buffer (in place) but must not partially overlap.
+ * w8a8_silu_bf16: y[i] = x / (1 + exp(-x)) correctly rounded to BF16, for
+ *   n elements, read from a table of all 65536 BF16 inputs that a small
+ *   kernel fills on the device (FP32 evaluation, FP64 for the rare inputs
+ *   whose FP32 value lies too close to a BF16 rounding midpoint) on the
+ *   caller's stream ahead of every call; x and y 16-byte aligned, n >= 0
+ *   and n % 8 == 0; x and y may be the same buffer (in place) but must not
+ *   partially overlap.
  *   Between FC1 and FC2 the block applies SiLU to the BF16 output of FC1
  *   ("MLX implementation and experiment report", "What the default
  *   preserves": SiLU rounding follows the original recipe).
@@ -166,6 +194,29 @@ int w8a8_last_hip_error(void);
  *   is not written.  Arguments and errors as w8a8_quantize_act.
  */
 int w8a8_silu_bf16(const uint16_t *x, uint16_t *y, int64_t n, void *stream);
+
+/*
+ * Gated-MLP glue for the fused gate/up projection of the pages' H3 shapes
+ * ("MLX implementation and experiment report", "Operator tuning": a fused
+ * gate/up GEMM 5376 -> 28672 feeding a down GEMM 14336 -> 5376; "What the
+ * default preserves": BF16 products and SiLU rounding as in the original).
+ *
+ * w8a8_swiglu_bf16: h BF16 [M, 2F] holds the gate g in its first F columns
+ *   and the up value u in the next F; y BF16 [M, F] = BF16(BF16(silu(g)) *
+ *   u), the SiLU as w8a8_silu_bf16 and the product (exact in FP32) rounded
+ *   once to nearest even.  h and y 16-byte aligned, F % 8 == 0, M >= 1; y
+ *   must not overlap h.
+ *
+ * w8a8_quantize_act_swiglu: w8a8_swiglu_bf16 followed by
+ *   w8a8_quantize_act of the [M, F] result in one pass over h (the SwiGLU
+ *   output is not written).  a_q INT8 [M, F] (8-byte aligned), a_scale
+ *   FP32 [M] (4-byte aligned); 8 <= F <= 90112.  Errors as
+ *   w8a8_quantize_act.
+ */
+int w8a8_swiglu_bf16(const uint16_t *h, uint16_t *y, int64_t M, int64_t F,
+                     void *stream);
+int w8a8_quantize_act_swiglu(const uint16_t *h, int64_t M, int64_t F,
+                             int8_t *a_q, float *a_scale, void *stream);
 int w8a8_pow2_renorm(const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                      void *stream);
 int w8a8_quantize_act_silu(const uint16_t *x, int64_t M, int64_t K,

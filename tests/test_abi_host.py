@@ -162,6 +162,36 @@ def test_glue_rejects():
                                       None) == SHAPE
 
 
+def test_weight_and_gated_glue_reject():
+    lib = B.lib()
+    qw = lib.w8a8_quantize_weight
+    assert qw(None, 4, 64, BUF["aq"], BUF["sa"], None) == NULL
+    assert qw(BUF["w"], 0, 64, BUF["aq"], BUF["sa"], None) == SHAPE
+    assert qw(BUF["w"], 4, 60, BUF["aq"], BUF["sa"], None) == SHAPE
+    assert qw(BUF["w"], 4, B.QUANT_MAX_K + 8, BUF["aq"], BUF["sa"],
+              None) == SHAPE
+    assert qw(BUF["w"] + 8, 4, 64, BUF["aq"], BUF["sa"], None) == ALIGN
+    assert qw(BUF["w"], 4, 64, BUF["w"] + 256, BUF["sa"], None) == ALIAS
+    cs = lib.w8a8_check_scales
+    assert cs(None, 4, BUF["out"], None) == NULL
+    assert cs(BUF["sw"], -1, BUF["out"], None) == SHAPE
+    assert cs(BUF["sw"] + 2, 4, BUF["out"], None) == ALIGN
+    assert cs(BUF["sw"], 4, BUF["out"] + 2, None) == ALIGN
+    assert cs(BUF["sw"], 4, BUF["sw"] + 8, None) == ALIAS
+    sg = lib.w8a8_swiglu_bf16
+    assert sg(None, BUF["out"], 2, 64, None) == NULL
+    assert sg(BUF["x"], BUF["out"], 2, 12, None) == SHAPE
+    assert sg(BUF["x"], BUF["out"], 0, 64, None) == SHAPE
+    assert sg(BUF["x"] + 2, BUF["out"], 2, 64, None) == ALIGN
+    assert sg(BUF["x"], BUF["x"] + 256, 2, 64, None) == ALIAS
+    qs = lib.w8a8_quantize_act_swiglu
+    assert qs(BUF["x"], 2, 64, None, BUF["sa"], None) == NULL
+    assert qs(BUF["x"], 2, B.QUANT_MAX_K + 8, BUF["aq"], BUF["sa"],
+              None) == SHAPE
+    assert qs(BUF["x"], 2, 64, BUF["aq"] + 4, BUF["sa"], None) == ALIGN
+    assert qs(BUF["x"], 2, 64, BUF["x"] + 128, BUF["sa"], None) == ALIAS
+
+
 def test_no_device_is_reported_without_a_gpu():
     """Valid arguments on a machine without a GPU: the device check, the
     last step before any launch, refuses.  Skipped where a GPU exists

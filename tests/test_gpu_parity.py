@@ -166,6 +166,85 @@ def test_pow2_renorm(orc, M, K):
 
 
 # ---------------------------------------------------------------------------
+# weight quantization, scale check, SwiGLU glue
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K", [(5376, 5376), (300, 21504), (7, 8),
+                                 (1000, 14336)])
+def test_quantize_weight(orc, N, K):
+    say(f"quantize_weight N={N} K={K}")
+    w = D.activations(N, K, seed=200 + N)
+    e = edge_rows(K)
+    w[: min(N, len(e))] = e[: min(N, len(e))]
+    if N > 7:
+        w[7] = 0          # all-zero row -> scale 1
+        w[8] = 0x8000     # all -0 -> scale 1
+    qg = Guarded((N, K), torch.int8)
+    sg = Guarded((N,), torch.float32)
+    B.quantize_weight(dev_bf16(w), out=(qg.t, sg.t))
+    torch.cuda.synchronize()
+    q_ref, s_ref = orc.quantize_weight(w)
+    qg.check()
+    sg.check()
+    assert np.array_equal(sg.t.cpu().numpy().view(np.uint32),
+                          s_ref.view(np.uint32))
+    assert np.array_equal(qg.t.cpu().numpy(), q_ref)
+    assert orc.check_scales(s_ref) == 0
+
+
+def test_check_scales(orc):
+    say("check_scales")
+    g = np.random.default_rng(5)
+    for N in (1, 100, 21504, 70001):
+        sw = np.exp(g.normal(-6, 0.3, N)).astype(np.float32)
+        if N >= 100:
+            idx = g.choice(N, 9, replace=False)
+            sw[idx] = [0.0, -0.0, -1.0, np.inf, -np.inf, np.nan, 1e-45,
+                       3.4e38, -2.5e-3]
+        bad = B.check_scales(dev(sw))
+        torch.cuda.synchronize()
+        assert int(bad.cpu().numpy()[0]) == orc.check_scales(sw)
+
+
+def test_swiglu_every_gate_value(orc):
+    # every finite BF16 gate against assorted up values, incl. overflow
+    say("swiglu over every finite BF16 gate")
+    gate = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    gate = gate[((gate >> 7) & 0xFF) != 0xFF]
+    gate = gate[: len(gate) // 8 * 8]
+    F = gate.size
+    g = np.random.default_rng(17)
+    ups = [D.to_bf16_bits((g.standard_normal(F) * 3).astype(np.float32)),
+           D.to_bf16_bits(np.full(F, 3e38, np.float32)),
+           np.array([0x0001, 0x8000, 0x0000, 0x7F7F], np.uint16).repeat(
+               F // 4)]
+    h = np.stack([np.concatenate([gate, u]) for u in ups])
+    y = host_bf16(B.swiglu(dev_bf16(h)))
+    assert np.array_equal(y, orc.swiglu_bf16(h))
+
+
+@pytest.mark.parametrize("M,F", [(4, 14336), (300, 14336), (3, 128),
+                                 (600, 5376), (2, 90112), (5, 8)])
+def test_quantize_act_swiglu(orc, M, F):
+    say(f"quantize_act_swiglu M={M} F={F}")
+    g = np.random.default_rng(M * F + 1)
+    h = D.to_bf16_bits((g.standard_normal((M, 2 * F)) * 4).astype(np.float32))
+    if M >= 6:
+        h[:6, :F] = edge_rows(F)
+        h[:6, F:] = edge_rows(F)[::-1]
+    qg = Guarded((M, F), torch.int8)
+    sg = Guarded((M,), torch.float32)
+    B.quantize_act_swiglu(dev_bf16(h), out=(qg.t, sg.t))
+    torch.cuda.synchronize()
+    q_ref, s_ref = orc.quantize_act(orc.swiglu_bf16(h))
+    qg.check()
+    sg.check()
+    assert np.array_equal(sg.t.cpu().numpy().view(np.uint32),
+                          s_ref.view(np.uint32))
+    assert np.array_equal(qg.t.cpu().numpy(), q_ref)
+
+
+# ---------------------------------------------------------------------------
 # GEMM
 # ---------------------------------------------------------------------------
 

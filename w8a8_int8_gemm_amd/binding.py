@@ -39,6 +39,10 @@ SIGNATURES = {
     "w8a8_last_hip_error": (_I, []),
     "w8a8_silu_bf16": (_I, [_P, _P, _I64, _P]),
     "w8a8_pow2_renorm": (_I, [_P, _P, _I64, _I64, _P]),
+    "w8a8_quantize_weight": (_I, [_P, _I64, _I64, _P, _P, _P]),
+    "w8a8_check_scales": (_I, [_P, _I64, _P, _P]),
+    "w8a8_swiglu_bf16": (_I, [_P, _P, _I64, _I64, _P]),
+    "w8a8_quantize_act_swiglu": (_I, [_P, _I64, _I64, _P, _P, _P]),
 }
 
 
@@ -215,3 +219,62 @@ def pow2_renorm(x, *, out=None, stream=None):
     _check("w8a8_pow2_renorm", lib().w8a8_pow2_renorm(
         _ptr(x), _ptr(y), M, K, _stream(stream)))
     return y
+
+
+def quantize_weight(w, *, out=None, stream=None):
+    """w: bf16 [N,K] -> (w_q int8 [N,K], w_scale float32 [N]), one scale
+    per output channel; all-zero rows get scale 1."""
+    torch = _torch()
+    _need(w, torch.bfloat16, 2, "w")
+    N, K = w.shape
+    if out is None:
+        q = torch.empty((N, K), dtype=torch.int8, device=w.device)
+        s = torch.empty((N,), dtype=torch.float32, device=w.device)
+    else:
+        q, s = out
+    _check("w8a8_quantize_weight", lib().w8a8_quantize_weight(
+        _ptr(w), N, K, _ptr(q), _ptr(s), _stream(stream)))
+    return q, s
+
+
+def check_scales(w_scale, *, out=None, stream=None):
+    """Device int32 [1]: how many scales are not finite and > 0."""
+    torch = _torch()
+    _need(w_scale, torch.float32, 1, "w_scale")
+    bad = (torch.empty((1,), dtype=torch.int32, device=w_scale.device)
+           if out is None else out)
+    _check("w8a8_check_scales", lib().w8a8_check_scales(
+        _ptr(w_scale), w_scale.numel(), _ptr(bad), _stream(stream)))
+    return bad
+
+
+def swiglu(h, *, out=None, stream=None):
+    """h: bf16 [M, 2F] (gate | up) -> bf16 [M, F]."""
+    torch = _torch()
+    _need(h, torch.bfloat16, 2, "h")
+    M, F2 = h.shape
+    if F2 % 2:
+        raise ValueError("h must have an even width (gate | up)")
+    y = (torch.empty((M, F2 // 2), dtype=torch.bfloat16, device=h.device)
+         if out is None else out)
+    _check("w8a8_swiglu_bf16", lib().w8a8_swiglu_bf16(
+        _ptr(h), _ptr(y), M, F2 // 2, _stream(stream)))
+    return y
+
+
+def quantize_act_swiglu(h, *, out=None, stream=None):
+    """h: bf16 [M, 2F] (gate | up) -> (a_q int8 [M,F], a_scale [M]) of
+    SwiGLU(h), in one pass."""
+    torch = _torch()
+    _need(h, torch.bfloat16, 2, "h")
+    M, F2 = h.shape
+    if F2 % 2:
+        raise ValueError("h must have an even width (gate | up)")
+    if out is None:
+        q = torch.empty((M, F2 // 2), dtype=torch.int8, device=h.device)
+        s = torch.empty((M,), dtype=torch.float32, device=h.device)
+    else:
+        q, s = out
+    _check("w8a8_quantize_act_swiglu", lib().w8a8_quantize_act_swiglu(
+        _ptr(h), M, F2 // 2, _ptr(q), _ptr(s), _stream(stream)))
+    return q, s

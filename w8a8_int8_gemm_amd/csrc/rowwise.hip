@@ -26,6 +26,7 @@
 // integer operations per pair of values replace the exp / reciprocal
 // evaluation.
 #include "internal.h"
+#include "rowwise.h"
 
 #include <mutex>
 #include <unordered_map>
@@ -38,7 +39,8 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;  // 4 waves of 64
 constexpr int kWaves = kThreads / 64;
 
-enum RowOp : int { OP_QUANT = 0, OP_RENORM = 2 };
+// OP_QUANT_W: per-output-channel weight rows; an all-zero row takes scale 1.
+enum RowOp : int { OP_QUANT = 0, OP_RENORM = 2, OP_QUANT_W = 3 };
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -160,10 +162,12 @@ __global__ __launch_bounds__(kThreads) void row_kernel(
     return;
   }
 
-  // Quantize: scale = amax / 127 (IEEE division), zero row -> scale 0.
+  // Quantize: scale = amax / 127 (IEEE division), zero row -> scale 0
+  // (activations) or 1 (weights, whose scales must be positive).
   const QuantRow R = quant_row(amax);
   const float s = R.s;
-  if (lane == 0 && part == 0) scale[row] = s;
+  if (lane == 0 && part == 0)
+    scale[row] = (OP == OP_QUANT_W && s == 0.0f) ? 1.0f : s;
   uint2 *qr = reinterpret_cast<uint2 *>(static_cast<int8_t *>(out) +
                                         row * (int64_t)K);
 #pragma unroll
@@ -217,11 +221,30 @@ __device__ __forceinline__ v4u silu_lut_chunk(const uint16_t *lut, v4u c) {
              silu_lut_pair(lut, c.z), silu_lut_pair(lut, c.w)};
 }
 
-// SiLU + per-token quantization.  The whole work group owns one row at a
+// Gated form (SwiGLU): BF16(silu(g)) from the table times the up value u;
+// both are BF16, so the binary32 product is exact and v_cvt_pk_bf16_f32
+// rounds it once (a product too small for binary32's normal range lies
+// below half the smallest BF16 subnormal unless it is exact, so it still
+// rounds as the exact value would).
+__device__ __forceinline__ uint32_t swiglu_pair(const uint16_t *lut,
+                                                uint32_t g, uint32_t u) {
+  const uint32_t s = silu_lut_pair(lut, g);
+  return pack_bf16x2(bf16_to_f32(s & 0xFFFFu) * bf16_to_f32(u & 0xFFFFu),
+                     bf16_to_f32(s >> 16) * bf16_to_f32(u >> 16));
+}
+
+__device__ __forceinline__ v4u swiglu_chunk(const uint16_t *lut, v4u g,
+                                            v4u u) {
+  return v4u{swiglu_pair(lut, g.x, u.x), swiglu_pair(lut, g.y, u.y),
+             swiglu_pair(lut, g.z, u.z), swiglu_pair(lut, g.w, u.w)};
+}
+
+// SiLU (or, GATED, SwiGLU over rows of gate | up, 2K wide) + per-token
+// quantization of the K results.  The whole work group owns one row at a
 // time (chunk j of the row is held by thread j mod 1024, CH chunks per
-// thread) and, for rows of up to 6 chunks per thread (K <= 49152), loads
-// its next row while it quantizes the current one.
-template <int CH>
+// thread) and, while two row buffers fit in registers, loads its next row
+// while it quantizes the current one.
+template <int CH, bool GATED>
 __global__ __launch_bounds__(kLutThreads, 1) void silu_quant_lut_kernel(
     const uint16_t *x, int8_t *q, float *__restrict__ scale, int64_t M,
     int K) {
@@ -233,18 +256,26 @@ __global__ __launch_bounds__(kLutThreads, 1) void silu_quant_lut_kernel(
   const int wave = threadIdx.x >> 6;
   const int chunks = K >> 3;
 
+  // Buffer b holds the row's chunks; with GATED, b[CH + i] is the up half
+  // of chunk i.
+  constexpr int NB = GATED ? 2 * CH : CH;
+  const int64_t stride = GATED ? 2 * (int64_t)K : K;
   auto load_row = [&](int64_t row, v4u *v) {
-    const v4u *xr = reinterpret_cast<const v4u *>(x + row * (int64_t)K);
+    const v4u *xr = reinterpret_cast<const v4u *>(x + row * stride);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int j = i * kLutThreads + threadIdx.x;
       v[i] = v4u{0, 0, 0, 0};
-      if (row < M && j < chunks) v[i] = __builtin_nontemporal_load(xr + j);
+      if (GATED) v[CH + i] = v4u{0, 0, 0, 0};
+      if (row < M && j < chunks) {
+        v[i] = __builtin_nontemporal_load(xr + j);
+        if (GATED) v[CH + i] = __builtin_nontemporal_load(xr + chunks + j);
+      }
     }
   };
 
-  constexpr bool kPrefetch = CH <= 6;  // two row buffers fit in registers
-  v4u cur[CH], nxt[kPrefetch ? CH : 1];
+  constexpr bool kPrefetch = NB <= 6;  // two row buffers fit in registers
+  v4u cur[NB], nxt[kPrefetch ? NB : 1];
   int64_t row = blockIdx.x;
   if (kPrefetch) load_row(row, cur);
   for (int it = 0; row < M; ++it, row += gridDim.x) {
@@ -255,7 +286,9 @@ __global__ __launch_bounds__(kLutThreads, 1) void silu_quant_lut_kernel(
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const v4u c = silu_lut_chunk(lut, cur[i]);  // zero chunks map to zero
+      // zero chunks map to zero
+      const v4u c = GATED ? swiglu_chunk(lut, cur[i], cur[CH + i])
+                          : silu_lut_chunk(lut, cur[i]);
       cur[i] = c;
       amax = fmaxf(amax, fmaxf(fmaxf(absmax_pair(c.x), absmax_pair(c.y)),
                                fmaxf(absmax_pair(c.z), absmax_pair(c.w))));
@@ -284,8 +317,48 @@ __global__ __launch_bounds__(kLutThreads, 1) void silu_quant_lut_kernel(
     }
     if (kPrefetch) {
 #pragma unroll
-      for (int i = 0; i < CH; ++i) cur[i] = nxt[kPrefetch ? i : 0];
+      for (int i = 0; i < NB; ++i) cur[i] = nxt[kPrefetch ? i : 0];
     }
+  }
+}
+
+// SwiGLU alone: chunk c of the output (row c / (F/8)) from the gate and up
+// chunks of its row.
+__global__ __launch_bounds__(kLutThreads, 1) void swiglu_lut_kernel(
+    const uint16_t *h, uint16_t *y, int64_t M, int64_t F) {
+  __shared__ uint32_t lut32[kLutEntries / 2];
+  lut_to_lds(lut32);
+  const uint16_t *lut = reinterpret_cast<const uint16_t *>(lut32);
+  const int64_t cpr = F / 8;  // output chunks per row
+  const v4u *hs = reinterpret_cast<const v4u *>(h);
+  v4u *ys = reinterpret_cast<v4u *>(y);
+  for (int64_t c = (int64_t)blockIdx.x * kLutThreads + threadIdx.x;
+       c < M * cpr; c += (int64_t)gridDim.x * kLutThreads) {
+    const int64_t row = c / cpr, j = c - row * cpr;
+    const v4u g = __builtin_nontemporal_load(hs + row * 2 * cpr + j);
+    const v4u u = __builtin_nontemporal_load(hs + row * 2 * cpr + cpr + j);
+    __builtin_nontemporal_store(swiglu_chunk(lut, g, u), ys + c);
+  }
+}
+
+// Number of scales that are not finite and > 0 (one work group).
+__global__ __launch_bounds__(1024) void check_scales_kernel(
+    const float *sw, int64_t N, int *bad) {
+  __shared__ int part[16];
+  int count = 0;
+  for (int64_t n = threadIdx.x; n < N; n += 1024) {
+    const float v = sw[n];
+    count += (v > 0.0f && v <= 0x1.fffffep127f) ? 0 : 1;  // NaN fails both
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) count += __shfl_xor(count, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = count;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) total += part[w];
+    *bad = total;
   }
 }
 
@@ -325,6 +398,32 @@ hipError_t build_silu_lut(hipStream_t stream) {
   return hipGetLastError();
 }
 
+// SwiGLU + quantization: h [M, 2F] -> codes [M, F].
+hipError_t launch_swiglu_quant_impl(const uint16_t *h, int8_t *q,
+                                    float *scale, int64_t M, int64_t F,
+                                    hipStream_t stream) {
+  hipError_t e = build_silu_lut(stream);
+  if (e != hipSuccess) return e;
+  const int chunks = (int)(F / 8);
+  const int ch = (chunks + kLutThreads - 1) / kLutThreads;
+  const dim3 grid((unsigned)(M < cu_count() ? M : cu_count()));
+#define W8A8_GLU_CASE(C)                                                     \
+  if (ch <= C) {                                                             \
+    hipLaunchKernelGGL((silu_quant_lut_kernel<C, true>), grid,              \
+                       dim3(kLutThreads), 0, stream, h, q, scale, M, (int)F); \
+    return hipGetLastError();                                                \
+  }
+  W8A8_GLU_CASE(1)
+  W8A8_GLU_CASE(2)
+  W8A8_GLU_CASE(3)
+  W8A8_GLU_CASE(4)
+  W8A8_GLU_CASE(6)
+  W8A8_GLU_CASE(8)
+  W8A8_GLU_CASE(11)
+#undef W8A8_GLU_CASE
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_silu_quant(const uint16_t *x, int8_t *q, float *scale,
                              int64_t M, int64_t K, hipStream_t stream) {
   hipError_t e = build_silu_lut(stream);
@@ -334,8 +433,8 @@ hipError_t launch_silu_quant(const uint16_t *x, int8_t *q, float *scale,
   const dim3 grid((unsigned)(M < cu_count() ? M : cu_count()));
 #define W8A8_LUT_CASE(C)                                                     \
   if (ch <= C) {                                                             \
-    hipLaunchKernelGGL((silu_quant_lut_kernel<C>), grid, dim3(kLutThreads), \
-                       0, stream, x, q, scale, M, (int)K);                   \
+    hipLaunchKernelGGL((silu_quant_lut_kernel<C, false>), grid,             \
+                       dim3(kLutThreads), 0, stream, x, q, scale, M, (int)K); \
     return hipGetLastError();                                                \
   }
   W8A8_LUT_CASE(1)
@@ -415,6 +514,35 @@ hipError_t launch_silu(const uint16_t *x, uint16_t *y, int64_t n,
   hipLaunchKernelGGL(silu_lut_kernel, dim3((unsigned)blocks),
                      dim3(kLutThreads), 0, stream, x, y, chunks);
   return hipGetLastError();
+}
+
+hipError_t launch_quantize_weight(const uint16_t *w, int8_t *q, float *sw,
+                                  int64_t N, int64_t K, hipStream_t stream) {
+  return launch_row_op<OP_QUANT_W>(w, q, sw, N, K, stream);
+}
+
+hipError_t launch_check_scales(const float *sw, int64_t N, int *bad,
+                               hipStream_t stream) {
+  hipLaunchKernelGGL(check_scales_kernel, dim3(1), dim3(1024), 0, stream, sw,
+                     N, bad);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const uint16_t *h, uint16_t *y, int64_t M, int64_t F,
+                         hipStream_t stream) {
+  hipError_t e = build_silu_lut(stream);
+  if (e != hipSuccess) return e;
+  const int64_t chunks = M * (F / 8);
+  int64_t blocks = (chunks + kLutThreads - 1) / kLutThreads;
+  if (blocks > cu_count()) blocks = cu_count();
+  hipLaunchKernelGGL(swiglu_lut_kernel, dim3((unsigned)blocks),
+                     dim3(kLutThreads), 0, stream, h, y, M, F);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_quant(const uint16_t *h, int8_t *q, float *scale,
+                               int64_t M, int64_t F, hipStream_t stream) {
+  return launch_swiglu_quant_impl(h, q, scale, M, F, stream);
 }
 
 }  // namespace w8a8

@@ -11,6 +11,7 @@
 #include <unordered_map>
 
 #include "internal.h"
+#include "rowwise.h"
 #include "w8a8.h"
 
 namespace {
@@ -231,6 +232,59 @@ int w8a8_linear(const uint16_t *x, const int8_t *w_q, const float *w_scale,
   GemmArgs g{aq, sa, w_q, w_scale, bias, y, W8A8_OUT_BF16,
              M,  N,  K,   gws,     gws_bytes};
   return hip_status(w8a8::launch_gemm(g, plan, s));
+}
+
+int w8a8_quantize_weight(const uint16_t *w, int64_t N, int64_t K,
+                         int8_t *w_q, float *w_scale, void *stream) {
+  int st = validate_quant(w, N, K, w_q, w_scale);
+  if (st != W8A8_OK) return st;
+  if ((st = check_device()) != W8A8_OK) return st;
+  return hip_status(w8a8::launch_quantize_weight(
+      w, w_q, w_scale, N, K, static_cast<hipStream_t>(stream)));
+}
+
+int w8a8_check_scales(const float *w_scale, int64_t N, int32_t *bad_count,
+                      void *stream) {
+  if (!w_scale || !bad_count) return W8A8_ERR_NULL;
+  if (N < 0 || N > kMaxRows) return W8A8_ERR_SHAPE;
+  if (!aligned(w_scale, 4) || !aligned(bad_count, 4)) return W8A8_ERR_ALIGN;
+  if (overlap(range_of(w_scale, N * 4), range_of(bad_count, 4)))
+    return W8A8_ERR_ALIAS;
+  int st = check_device();
+  if (st != W8A8_OK) return st;
+  return hip_status(w8a8::launch_check_scales(
+      w_scale, N, bad_count, static_cast<hipStream_t>(stream)));
+}
+
+int w8a8_swiglu_bf16(const uint16_t *h, uint16_t *y, int64_t M, int64_t F,
+                     void *stream) {
+  if (!h || !y) return W8A8_ERR_NULL;
+  if (M < 1 || M > kMaxRows || F < 8 || F % 8 != 0 || F > kMaxRows / 2)
+    return W8A8_ERR_SHAPE;
+  if (!aligned(h, 16) || !aligned(y, 16)) return W8A8_ERR_ALIGN;
+  if (overlap(range_of(h, M * F * 4), range_of(y, M * F * 2)))
+    return W8A8_ERR_ALIAS;
+  int st = check_device();
+  if (st != W8A8_OK) return st;
+  return hip_status(
+      w8a8::launch_swiglu(h, y, M, F, static_cast<hipStream_t>(stream)));
+}
+
+int w8a8_quantize_act_swiglu(const uint16_t *h, int64_t M, int64_t F,
+                             int8_t *a_q, float *a_scale, void *stream) {
+  if (!h || !a_q || !a_scale) return W8A8_ERR_NULL;
+  if (M < 1 || M > kMaxRows || F < 8 || F % 8 != 0 || F > kQuantMaxK)
+    return W8A8_ERR_SHAPE;
+  if (!aligned(h, 16) || !aligned(a_q, 8) || !aligned(a_scale, 4))
+    return W8A8_ERR_ALIGN;
+  const Range rh = range_of(h, M * F * 4), rq = range_of(a_q, M * F),
+              rs = range_of(a_scale, M * 4);
+  if (overlap(rh, rq) || overlap(rh, rs) || overlap(rq, rs))
+    return W8A8_ERR_ALIAS;
+  int st = check_device();
+  if (st != W8A8_OK) return st;
+  return hip_status(w8a8::launch_swiglu_quant(
+      h, a_q, a_scale, M, F, static_cast<hipStream_t>(stream)));
 }
 
 int w8a8_silu_bf16(const uint16_t *x, uint16_t *y, int64_t n, void *stream) {
