@@ -18,7 +18,7 @@ Inputs and weights are resident in HBM before timing starts.  Reported:
   cpu_baseline = the CPU oracle timed on a bounded row sample;
   bf16_baseline (context) = torch's BF16 linear (hipBLASLt) on the same
                shapes.
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 0-4]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 0-6]
        [--fused-qkv]
 """
 from __future__ import annotations
@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--config", type=int, default=4, choices=range(5))
+    ap.add_argument("--config", type=int, default=4, choices=range(7))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
@@ -128,6 +128,9 @@ def main():
         dblk = {p.name: BL.upload_proj(p, params[p.name], dev)
                 for p in wl.projs}
         if args.fused_qkv and not single:
+            if wl.o_input != "x":
+                raise SystemExit("--fused-qkv needs a workload whose "
+                                 "attention output projection reads X")
             dblk = BL.fuse_qkv(dblk)
         blocks.append(dblk)
         if rows is not None:
@@ -136,13 +139,7 @@ def main():
                 pp = params[p.name]
                 chk_out = {p.name: orc.linear(chk_x, pp.w, pp.sw, pp.bias)}
             else:
-                chk_out = {}
-                for n in ("q", "k", "v", "o", "fc1"):
-                    pp = params[n]
-                    chk_out[n] = orc.linear(chk_x, pp.w, pp.sw, pp.bias)
-                h = orc.silu_bf16(chk_out["fc1"])
-                pp = params["fc2"]
-                chk_out["fc2"] = orc.linear(h, pp.w, pp.sw, pp.bias)
+                chk_out = oracle_block_rows(orc, wl, params, chk_x)
                 if b + 1 < wl.blocks:
                     chk_x = orc.pow2_renorm(chk_out["fc2"])
         del params
@@ -153,7 +150,8 @@ def main():
 
     x0 = BL.to_device_bf16(x0_host, dev)
     xbuf = [torch.empty_like(x0), torch.empty_like(x0)]
-    runner = (BL.BlockRunner(M, dev, fused_qkv=args.fused_qkv)
+    runner = (BL.BlockRunner(M, dev, fused_qkv=args.fused_qkv,
+                             projs=wl.projs, mlp=wl.mlp, o_input=wl.o_input)
               if not single else None)
     if single:
         p0 = wl.projs[0]
@@ -336,11 +334,18 @@ def bf16_baseline(torch, D, BL, wl, x0, blk, dev, warmup, reps):
         if len(blk) == 1:
             n = next(iter(blk))
             return F.linear(x0, ws[n], bs[n])
+        out = {}
         for n in blk:
-            if n not in ("fc1", "fc2"):
-                F.linear(x0, ws[n], bs[n])
+            if n not in ("o", "fc1", "fc2"):
+                out[n] = F.linear(x0, ws[n], bs[n])
+        F.linear(out["v"] if wl.o_input == "v" else x0, ws["o"], bs["o"])
         h = F.linear(x0, ws["fc1"], bs["fc1"])
-        return F.linear(F.silu(h), ws["fc2"], bs["fc2"])
+        if wl.mlp == "swiglu":
+            g, u = h.chunk(2, dim=-1)
+            h = F.silu(g) * u
+        else:
+            h = F.silu(h)
+        return F.linear(h, ws["fc2"], bs["fc2"])
 
     for _ in range(warmup + 1):
         run()
@@ -358,7 +363,24 @@ def bf16_baseline(torch, D, BL, wl, x0, blk, dev, warmup, reps):
     return {"tflops": round(tflops, 2), "ms_per_block": round(ms, 4),
             "pct_bf16_peak": round(100 * tflops / BF16_PEAK_TFLOPS, 2),
             "what": "torch.nn.functional.linear, BF16 weights, one block "
-                    "(SiLU included)"}
+                    "(SiLU or SwiGLU included)"}
+
+
+def oracle_block_rows(orc, wl, params, x_rows):
+    """One block's BF16 outputs for some token rows through the oracle
+    (rows are independent through every step of the block)."""
+    out = {}
+    for n in ("q", "k", "v", "fc1"):
+        pp = params[n]
+        out[n] = orc.linear(x_rows, pp.w, pp.sw, pp.bias)
+    pp = params["o"]
+    out["o"] = orc.linear(out["v"] if wl.o_input == "v" else x_rows, pp.w,
+                          pp.sw, pp.bias)
+    h = (orc.swiglu_bf16(out["fc1"]) if wl.mlp == "swiglu"
+         else orc.silu_bf16(out["fc1"]))
+    pp = params["fc2"]
+    out["fc2"] = orc.linear(h, pp.w, pp.sw, pp.bias)
+    return out
 
 
 def cpu_baseline(orc, D, wl, x0_host, seconds, threads):
@@ -366,26 +388,17 @@ def cpu_baseline(orc, D, wl, x0_host, seconds, threads):
     projections; rows are doubled until the run lasts `seconds`/4, then one
     final timed run with about `seconds` of work."""
     params = D.block_params(wl, 0, threads=threads)
-    K = D.HIDDEN
 
     def run(R):
         x = x0_host[:R]
-        macs = 0
         t = time.perf_counter()
         if len(wl.projs) == 1:
             p = wl.projs[0]
             pp = params[p.name]
             orc.linear(x, pp.w, pp.sw, pp.bias)
-            macs += R * p.N * p.K
         else:
-            for n in ("q", "k", "v", "o", "fc1"):
-                pp = params[n]
-                y = orc.linear(x, pp.w, pp.sw, pp.bias)
-                macs += R * pp.w.shape[0] * K
-            h = orc.silu_bf16(y)
-            pp = params["fc2"]
-            orc.linear(h, pp.w, pp.sw, pp.bias)
-            macs += R * pp.w.shape[0] * pp.w.shape[1]
+            oracle_block_rows(orc, wl, params, x)
+        macs = sum(R * p.N * p.K for p in wl.projs)
         return time.perf_counter() - t, macs
 
     R = 4

@@ -395,15 +395,19 @@ def test_gemm_deterministic():
 # full-size DiT blocks, sampled rows
 # ---------------------------------------------------------------------------
 
-def oracle_block_rows(orc, x_rows, params):
+def oracle_block_rows(orc, x_rows, params, mlp="silu", o_input="x"):
     """Oracle of the block's data flow on a subset of token rows."""
     out = {}
     q, s = orc.quantize_act(x_rows)
     out["xq"], out["xs"] = q, s
-    for n in ("q", "k", "v", "o", "fc1"):
+    for n in ("q", "k", "v", "fc1"):
         p = params[n]
         out[n] = orc.linear(x_rows, p.w, p.sw, p.bias)
-    h = orc.silu_bf16(out["fc1"])
+    p = params["o"]
+    out["o"] = orc.linear(out["v"] if o_input == "v" else x_rows, p.w, p.sw,
+                          p.bias)
+    h = (orc.swiglu_bf16(out["fc1"]) if mlp == "swiglu"
+         else orc.silu_bf16(out["fc1"]))
     out["hq"], out["hs"] = orc.quantize_act(h)
     p = params["fc2"]
     out["fc2"] = orc.linear(h, p.w, p.sw, p.bias)
@@ -422,19 +426,23 @@ def test_config0_single_projection(orc):
     assert np.array_equal(host_bf16(y), orc.linear(x, pp.w, pp.sw, pp.bias))
 
 
-@pytest.mark.parametrize("config", [1, 2, 3])
+# configs 1-3: the block at 4096, 19077 and 37503 tokens; 5: the pages' H3
+# operator shapes (Q/K/V 5376 -> 7168, O fed by V, SwiGLU over a fused
+# gate | up FC1 5376 -> 28672, FC2 14336 -> 5376) at 19077 tokens.
+@pytest.mark.parametrize("config", [1, 2, 3, 5])
 def test_block_sampled_rows(orc, config):
     wl = D.WORKLOADS[config]
     say(f"block config {config}: {wl.name} M={wl.M}")
     params = D.block_params(wl, 0)
     projs = {p.name: BL.upload_proj(p, params[p.name]) for p in wl.projs}
     x = D.activations(wl.M, D.HIDDEN, wl.seed)
-    runner = BL.BlockRunner(wl.M)
+    runner = BL.BlockRunner(wl.M, projs=wl.projs, mlp=wl.mlp,
+                            o_input=wl.o_input)
     out = runner.run(dev_bf16(x), projs)
     torch.cuda.synchronize()
     rows = D.row_sample(wl.M, 24, wl.seed)
     ri = torch.from_numpy(rows).cuda()
-    ref = oracle_block_rows(orc, x[rows], params)
+    ref = oracle_block_rows(orc, x[rows], params, wl.mlp, wl.o_input)
     assert np.array_equal(runner.xq[0][ri].cpu().numpy(), ref["xq"])
     assert np.array_equal(runner.xs[0][ri].cpu().numpy().view(np.uint32),
                           ref["xs"].view(np.uint32))

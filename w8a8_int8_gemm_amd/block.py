@@ -10,7 +10,9 @@ BF16 value, rounded per the original recipe).  Attention and the norms are
 not part of the projection path, so the synthetic block feeds its input X
 to O and FC1 as well; that keeps four quantizations per block, as in the
 model.  Everything here is a sequence of library calls on one stream;
-outputs and scratch are preallocated once per token count.
+outputs and scratch are preallocated once per token count.  The pages' own
+H3 shapes (see datagen) use SwiGLU over a fused gate | up FC1 and feed V's
+output (the attention result's shape) to the attention output projection.
 
 Fused QKV (optional): the Q, K and V weights concatenated along the output
 channels, [3N, K] with their scales and biases, run as one GEMM on the
@@ -72,34 +74,45 @@ def fuse_qkv(projs: dict) -> dict:
 
 
 class BlockRunner:
-    """Preallocated buffers for one token count M; ``run`` enqueues the
+    """Preallocated buffers for one token count M and one block layout
+    (``projs``: the workload's six projections; ``mlp``: "silu", or
+    "swiglu" for a fused gate | up FC1; ``o_input``: "x", or "v" to feed
+    V's output to the attention output projection).  ``run`` enqueues the
     block's kernels on the current stream (or ``stream``).  ``on_gemm`` is
     called around every GEMM launch (for per-kernel event timing)."""
 
-    def __init__(self, M: int, device="cuda", fused_qkv: bool = False):
+    def __init__(self, M: int, device="cuda", fused_qkv: bool = False,
+                 projs=D.BLOCK_PROJS, mlp: str = "silu", o_input: str = "x"):
         import torch
-        self.M = M
-        H, F = D.HIDDEN, D.FFN
+        if fused_qkv and o_input != "x":
+            raise ValueError("fused QKV needs the block input as O's input")
+        self.M, self.mlp, self.o_input = M, mlp, o_input
+        shape = {p.name: (p.N, p.K) for p in projs}
+        H = shape["q"][1]  # block width
         e = lambda *s, dt: torch.empty(s, dtype=dt, device=device)
+        # X quantized for Q/K/V, for O (when it reads X) and for FC1
         self.xq = [e(M, H, dt=torch.int8) for _ in range(3)]
         self.xs = [e(M, dt=torch.float32) for _ in range(3)]
-        self.hq = e(M, F, dt=torch.int8)
+        self.oq = (e(M, shape["o"][1], dt=torch.int8) if o_input == "v"
+                   else None)
+        self.hq = e(M, shape["fc2"][1], dt=torch.int8)
         self.hs = e(M, dt=torch.float32)
-        self.out = {n: e(M, H, dt=torch.bfloat16) for n in ("o", "fc2")}
+        self.out = {n: e(M, shape[n][0], dt=torch.bfloat16)
+                    for n in ("o", "fc1", "fc2")}
         if fused_qkv:
-            self.out["qkv"] = e(M, 3 * H, dt=torch.bfloat16)
+            nq = shape["q"][0]
+            self.out["qkv"] = e(M, 3 * nq, dt=torch.bfloat16)
             for i, n in enumerate(("q", "k", "v")):
-                self.out[n] = self.out["qkv"][:, i * H:(i + 1) * H]
+                self.out[n] = self.out["qkv"][:, i * nq:(i + 1) * nq]
         else:
             for n in ("q", "k", "v"):
-                self.out[n] = e(M, H, dt=torch.bfloat16)
-        self.out["fc1"] = e(M, F, dt=torch.bfloat16)
-        ws = max(B.workspace_bytes(M, H, H), B.workspace_bytes(M, F, H),
-                 B.workspace_bytes(M, H, F), B.workspace_bytes(M, 3 * H, H))
-        self.ws = e(max(ws, 256), dt=torch.uint8)
+                self.out[n] = e(M, shape[n][0], dt=torch.bfloat16)
+        need = [B.workspace_bytes(M, N, K) for N, K in shape.values()]
+        need.append(B.workspace_bytes(M, 3 * shape["q"][0], H))
+        self.ws = e(max(max(need), 256), dt=torch.uint8)
 
     def run(self, x, projs: dict, stream=None, on_gemm=None):
-        """x: bf16 [M, 5376].  Returns the dict of BF16 outputs."""
+        """x: bf16 [M, H].  Returns the dict of BF16 outputs."""
         def gemm(name, q, s):
             p = projs[name]
             if on_gemm:
@@ -115,12 +128,22 @@ class BlockRunner:
         for n in (("qkv",) if "qkv" in projs else ("q", "k", "v")):
             gemm(n, self.xq[0], self.xs[0])
         # attention output projection and FC1 quantize their own inputs.
-        B.quantize_act(x, out=(self.xq[1], self.xs[1]), stream=stream)
-        gemm("o", self.xq[1], self.xs[1])
+        if self.o_input == "v":
+            B.quantize_act(self.out["v"], out=(self.oq, self.xs[1]),
+                           stream=stream)
+            gemm("o", self.oq, self.xs[1])
+        else:
+            B.quantize_act(x, out=(self.xq[1], self.xs[1]), stream=stream)
+            gemm("o", self.xq[1], self.xs[1])
         B.quantize_act(x, out=(self.xq[2], self.xs[2]), stream=stream)
         gemm("fc1", self.xq[2], self.xs[2])
-        # FC2 input: SiLU of FC1's BF16 output, quantized in the same pass.
-        B.quantize_act(self.out["fc1"], silu=True, out=(self.hq, self.hs),
-                       stream=stream)
+        # FC2 input: SiLU (or SwiGLU of gate | up) of FC1's BF16 output,
+        # quantized in the same pass.
+        if self.mlp == "swiglu":
+            B.quantize_act_swiglu(self.out["fc1"], out=(self.hq, self.hs),
+                                  stream=stream)
+        else:
+            B.quantize_act(self.out["fc1"], silu=True,
+                           out=(self.hq, self.hs), stream=stream)
         gemm("fc2", self.hq, self.hs)
         return self.out

@@ -25,6 +25,15 @@ frame counts of the FastVideo pull request ("Test Results": 124 frames
 give 37 video latent frames and 207 audio latent frames): one video latent
 frame holds (H/32)*(W/32) tokens, so 544x960 gives 37*510 + 207 = 19077
 tokens and 768x1344 gives 37*1008 + 207 = 37503.
+
+A second shape set follows the pages' own H3 operator shapes ("MLX
+implementation and experiment report", "Operator tuning": QKV 5376 ->
+21504, i.e. 3 x 7168 = 56 heads x 128, a fused gate/up projection 5376 ->
+28672 and a down projection 14336 -> 5376): Q, K, V map 5376 -> 7168, the
+attention output 7168 -> 5376, FC1 (gate | up) 5376 -> 28672 and FC2
+14336 -> 5376 after SwiGLU.  Attention is not on the projection path, so
+that block feeds V's output to the attention output projection as the
+stand-in for the attention result (same shape).
 """
 from __future__ import annotations
 
@@ -35,6 +44,8 @@ import numpy as np
 
 HIDDEN = 5376
 FFN = 21504
+ATTN = 7168       # 56 heads x 128 (page shapes)
+GATE_UP = 28672   # fused gate | up (page shapes)
 
 KIND_X, KIND_W, KIND_SW, KIND_BIAS = 0, 1, 2, 3
 
@@ -57,6 +68,16 @@ BLOCK_PROJS = (
 )
 
 
+PAGE_BLOCK_PROJS = (
+    Proj("q", 0, ATTN, HIDDEN),
+    Proj("k", 1, ATTN, HIDDEN),
+    Proj("v", 2, ATTN, HIDDEN),
+    Proj("o", 3, HIDDEN, ATTN),
+    Proj("fc1", 4, GATE_UP, HIDDEN),
+    Proj("fc2", 5, HIDDEN, GATE_UP // 2),
+)
+
+
 def tokens(height: int, width: int, video_latent_frames: int = 37,
            audio_tokens: int = 207) -> int:
     """Packed audio/video token count of one DiT input."""
@@ -71,6 +92,8 @@ class Workload:
     projs: tuple
     blocks: int
     seed: int
+    mlp: str = "silu"     # FC1 -> FC2 glue: "silu" or "swiglu" (gate | up)
+    o_input: str = "x"    # attention output projection input: "x" or "v"
 
 
 WORKLOADS = {
@@ -80,6 +103,10 @@ WORKLOADS = {
     3: Workload("dit_block_768x1344_124f", tokens(768, 1344), BLOCK_PROJS, 1, 3),
     4: Workload("dit_sweep_300_linears_544x960_124f", tokens(544, 960),
                 BLOCK_PROJS, 50, 4),
+    5: Workload("dit_block_h3_page_shapes_544x960_124f", tokens(544, 960),
+                PAGE_BLOCK_PROJS, 1, 5, "swiglu", "v"),
+    6: Workload("dit_sweep_300_linears_h3_page_shapes_544x960_124f",
+                tokens(544, 960), PAGE_BLOCK_PROJS, 50, 6, "swiglu", "v"),
 }
 
 
