@@ -9,12 +9,14 @@ input, all of it in the library's HIP kernels on one stream:
   feeds the next block.
 Inputs and weights are resident in HBM before timing starts.  Reported:
   value      = sum of 2*M*N*K over the step's GEMMs / step time (TOPS),
-               quantization and glue time included;
+               quantization and glue time included, from K steps timed
+               without per-call events;
   roofline   = the INT8 GEMM alone (one w8a8_gemm call: the main kernel
                launch and, where the last wave of tiles is short, its split-K
                tail launch and reduction): algorithmic ops / average call
-               time (HIP events around every call, on the launch stream),
-               against the dense INT8 MFMA peak of 5.0 POP/s;
+               time (HIP events around every call, on the launch stream,
+               over K more steps), against the dense INT8 MFMA peak of
+               5.0 POP/s;
   cpu_baseline = the CPU oracle timed on a bounded row sample;
   bf16_baseline (context) = torch's BF16 linear (hipBLASLt) on the same
                shapes.
@@ -199,19 +201,29 @@ def main():
         step(False)
     torch.cuda.synchronize()
 
+    # Timed region 1: the steps alone (value).  An event recorded between
+    # two kernels costs a few microseconds of queue time, so the per-call
+    # GEMM events are kept out of this region.
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    all_gemm = []
     torch.cuda.synchronize()
     start.record()
     for _ in range(args.steps):
-        out = step(True)
-        all_gemm.append(gemm_events)
+        out = step(False)
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / max(args.steps, 1)
     tops = ops_per_step / (ms_per_step * 1e-3) / 1e12
+
+    # Timed region 2: the same steps with HIP events around every GEMM call
+    # on the launch stream (roofline: average duration of one call).
+    all_gemm = []
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        out = step(True)
+        all_gemm.append(gemm_events)
+    torch.cuda.synchronize()
 
     # per-launch GEMM durations
     gemm_ms = 0.0

@@ -322,11 +322,16 @@ def test_linear(orc, M, N, K):
     assert np.array_equal(y, orc.linear(x, w, sw, b))
 
 
-@pytest.mark.parametrize("M,N,K", [(4097, 4096, 1664), (4097, 4096, 1024)])
+@pytest.mark.parametrize("M,N,K", [(4097, 4096, 1664), (4097, 4096, 1024),
+                                   (4396, 3968, 2048), (65541, 128, 1024)])
 def test_gemm_tail_split(orc, M, N, K):
-    # 17 x 16 tiles of 256 x 256: one full wave of 256 tiles, then the 16
-    # tiles of the one-row last token tile split K (26 stages in 3 slices of
-    # 8/9/9, or 16 stages in 2) and summed by the tail reduction.
+    # 4097 x 4096: 17 x 16 tiles of 256 x 256: one full wave of 256 tiles,
+    # then the 16 tiles of the one-row last token tile split K (26 stages in
+    # 3 slices of 8/9/9, or 16 stages in 2) and summed by the tail reduction.
+    # 4396 x 3968: 18 x 16 tiles whose last token tile holds 44 rows and last
+    # channel tile 128 channels; 32 tail tiles in 4 slices.  65541 x 128:
+    # one channel tile, half of it past N, 257 tiles, the last (5 rows)
+    # split in 2.
     ws = B.workspace_bytes(M, N, K)
     say(f"gemm tail split M={M} N={N} K={K} workspace={ws}")
     assert ws > 0
