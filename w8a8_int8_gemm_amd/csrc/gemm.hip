@@ -313,10 +313,6 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(KernelArgs p) {
   };
   // Interleave: after every MFMAS/READS MFMAs, one fragment read.
   auto interleave = [&]() {
-#ifndef W8A8_INTERLEAVE
-#define W8A8_INTERLEAVE 0
-#endif
-#if W8A8_INTERLEAVE == 0
 #pragma unroll
     for (int r = 0; r < READS; ++r) {
       __builtin_amdgcn_sched_group_barrier(0x008, MFMAS / READS, 0);
@@ -324,21 +320,6 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(KernelArgs p) {
     }
     if constexpr (MFMAS % READS != 0)
       __builtin_amdgcn_sched_group_barrier(0x008, MFMAS % READS, 0);
-#elif W8A8_INTERLEAVE == 1
-    __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, MFMAS, 0);
-#elif W8A8_INTERLEAVE == 2
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - 1, 0);
-#elif W8A8_INTERLEAVE == 3
-#pragma unroll
-    for (int r = 0; r < READS / 2; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - READS / 2, 0);
-#endif
   };
   // One stage: its KS k-steps; the last one crosses into stage kt+1.
   // Every stage but the last requests one stage's loads after its barrier:
