@@ -75,25 +75,51 @@ __device__ __noinline__ float quant_biased_exact(float x, float s) {
 }
 
 // Four BF16 values (two packed pairs) -> four INT8 codes in one dword.
+// The closeness test runs on the four values together; in the rare group
+// where one is close to a half-integer (or the row needs the exact path),
+// every code of the group comes from the division.
 __device__ __forceinline__ uint32_t quant4(uint32_t p01, uint32_t p23,
                                            const QuantRow &R) {
   const float f[4] = {bf16_to_f32(p01 & 0xFFFFu), bf16_to_f32(p01 >> 16),
                       bf16_to_f32(p23 & 0xFFFFu), bf16_to_f32(p23 >> 16)};
-  uint32_t out = 0;
+  float u[4], d[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    float u = R.fast ? fmaf(f[e], R.r, 128.0f) : 0.5f;
-    const float fr = __builtin_amdgcn_fractf(u);
-    if (!(fabsf(fr - 0.5f) > 0x1p-14f)) u = quant_biased_exact(f[e], R.s);
-    // round to the nearest integer in [0, 255] and insert as byte e
-    out = __builtin_amdgcn_cvt_pk_u8_f32(u, e, out);
+    u[e] = fmaf(f[e], R.r, 128.0f);
+    d[e] = fabsf(__builtin_amdgcn_fractf(u[e]) - 0.5f);
   }
+  const float dmin = fminf(fminf(d[0], d[1]), fminf(d[2], d[3]));
+  if (!R.fast || !(dmin > 0x1p-14f)) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = quant_biased_exact(f[e], R.s);
+  }
+  uint32_t out = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)  // nearest integer in [0, 255] as byte e
+    out = __builtin_amdgcn_cvt_pk_u8_f32(u[e], e, out);
   return out ^ 0x80808080u;  // biased byte -> two's complement code
 }
 
-__device__ __forceinline__ float absmax_pair(uint32_t packed) {
-  return fmaxf(fabsf(bf16_to_f32(packed & 0xFFFFu)),
-               fabsf(bf16_to_f32(packed >> 16)));
+// Row maximum of |x| on the BF16 bit patterns: for finite values the
+// magnitude bits (sign cleared) order like the magnitudes, so a packed
+// 16-bit unsigned max over two values per dword finds the largest |x|
+// exactly; the two halves are merged once per row.
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ us2 mag_max4(us2 m, v4u c) {
+  const uint32_t k = 0x7FFF7FFFu;
+  const us2 a = __builtin_bit_cast(us2, c.x & k);
+  const us2 b = __builtin_bit_cast(us2, c.y & k);
+  const us2 d = __builtin_bit_cast(us2, c.z & k);
+  const us2 e = __builtin_bit_cast(us2, c.w & k);
+  return __builtin_elementwise_max(
+      __builtin_elementwise_max(m, a),
+      __builtin_elementwise_max(__builtin_elementwise_max(b, d), e));
+}
+
+__device__ __forceinline__ float mag_to_f32(us2 m) {
+  const uint32_t hi = m.x > m.y ? m.x : m.y;
+  return __uint_as_float(hi << 16);
 }
 
 __device__ __forceinline__ uint32_t renorm_pair(uint32_t packed, int e) {
@@ -117,19 +143,15 @@ __global__ __launch_bounds__(kThreads) void row_kernel(
   const v4u *xr = reinterpret_cast<const v4u *>(x + row * (int64_t)K);
 
   v4u v[CH];
-  float amax = 0.0f;
+  us2 mag = us2{0, 0};
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int j = (i * WPR + part) * 64 + lane;
     v[i] = v4u{0, 0, 0, 0};
-    if (row_ok && j < chunks) {
-      const v4u c = __builtin_nontemporal_load(xr + j);
-      v[i] = c;
-      amax = fmaxf(amax, fmaxf(fmaxf(absmax_pair(c.x), absmax_pair(c.y)),
-                               fmaxf(absmax_pair(c.z), absmax_pair(c.w))));
-    }
+    if (row_ok && j < chunks) v[i] = __builtin_nontemporal_load(xr + j);
+    mag = mag_max4(mag, v[i]);  // masked chunks are zero
   }
-  amax = wave_max(amax);
+  float amax = wave_max(mag_to_f32(mag));
   if (WPR > 1) {
     if (lane == 0) part_max[wave] = amax;
     __syncthreads();
@@ -242,8 +264,7 @@ __device__ __forceinline__ v4u swiglu_chunk(const uint16_t *lut, v4u g,
 // SiLU (or, GATED, SwiGLU over rows of gate | up, 2K wide) + per-token
 // quantization of the K results.  The whole work group owns one row at a
 // time (chunk j of the row is held by thread j mod 1024, CH chunks per
-// thread) and, while two row buffers fit in registers, loads its next row
-// while it quantizes the current one.
+// thread) and loads the following rows while it quantizes the current one.
 template <int CH, bool GATED>
 __global__ __launch_bounds__(kLutThreads, 1) void silu_quant_lut_kernel(
     const uint16_t *x, int8_t *q, float *__restrict__ scale, int64_t M,
@@ -274,26 +295,32 @@ __global__ __launch_bounds__(kLutThreads, 1) void silu_quant_lut_kernel(
     }
   };
 
-  constexpr bool kPrefetch = NB <= 6;  // two row buffers fit in registers
-  v4u cur[NB], nxt[kPrefetch ? NB : 1];
+  // Rows loaded ahead of the one being quantized: two while three row
+  // buffers fit in registers, else one, else none.  With one work group per
+  // CU, the loads in flight per CU are what keeps HBM busy.
+  constexpr int kDepth = NB <= 4 ? 2 : (NB <= 6 ? 1 : 0);
+  v4u cur[NB], nxt[kDepth >= 1 ? NB : 1], nxt2[kDepth >= 2 ? NB : 1];
   int64_t row = blockIdx.x;
-  if (kPrefetch) load_row(row, cur);
-  for (int it = 0; row < M; ++it, row += gridDim.x) {
-    if (kPrefetch)
-      load_row(row + gridDim.x, nxt);  // rows past M load nothing
+  const int64_t g = gridDim.x;
+  if (kDepth >= 1) load_row(row, cur);
+  if (kDepth >= 2) load_row(row + g, nxt);  // rows past M load nothing
+  for (int it = 0; row < M; ++it, row += g) {
+    if (kDepth == 2)
+      load_row(row + 2 * g, nxt2);
+    else if (kDepth == 1)
+      load_row(row + g, nxt);
     else
       load_row(row, cur);
-    float amax = 0.0f;
+    us2 mag = us2{0, 0};
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       // zero chunks map to zero
       const v4u c = GATED ? swiglu_chunk(lut, cur[i], cur[CH + i])
                           : silu_lut_chunk(lut, cur[i]);
       cur[i] = c;
-      amax = fmaxf(amax, fmaxf(fmaxf(absmax_pair(c.x), absmax_pair(c.y)),
-                               fmaxf(absmax_pair(c.z), absmax_pair(c.w))));
+      mag = mag_max4(mag, c);
     }
-    amax = wave_max(amax);
+    float amax = wave_max(mag_to_f32(mag));
     if (lane == 0) part_max[it & 1][wave] = amax;
     __syncthreads();
     amax = part_max[it & 1][0];
@@ -315,9 +342,13 @@ __global__ __launch_bounds__(kLutThreads, 1) void silu_quant_lut_kernel(
         qr[j] = o;
       }
     }
-    if (kPrefetch) {
+    if (kDepth >= 1) {
 #pragma unroll
-      for (int i = 0; i < NB; ++i) cur[i] = nxt[kPrefetch ? i : 0];
+      for (int i = 0; i < NB; ++i) cur[i] = nxt[kDepth >= 1 ? i : 0];
+    }
+    if (kDepth >= 2) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) nxt[i] = nxt2[kDepth >= 2 ? i : 0];
     }
   }
 }
