@@ -383,39 +383,42 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(KernelArgs p) {
     int8_t *region = smem + wave * (C::WM * ROWB);
     const int mb = m0 + wave_m * C::WM;
     const int nb = n0 + wave_n * C::WN;
-    const bool has_bias = p.bias != nullptr;
+    // N is a multiple of 128 and so is nb: a wave's 128 channels are all
+    // inside N or all past it (then nothing of this wave is stored).
+    if (nb < p.N) {
+      float sam[C::TM];
 #pragma unroll
-    for (int j = 0; j < C::TM; ++j) {
-      const int r = j * 32 + (lane & 31);
-      const int m = mb + r;
-      const float sam = m < p.M ? p.sa[m] : 0.0f;
+      for (int j = 0; j < C::TM; ++j) {
+        const int m = mb + j * 32 + (lane & 31);
+        sam[j] = m < p.M ? p.sa[m] : 0.0f;
+      }
 #pragma unroll
       for (int i = 0; i < C::TN; ++i) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int nl = i * 32 + 8 * g + 4 * (lane >> 5);
           const int n = nb + nl;
-          uint2 v = make_uint2(0, 0);
-          if (n < p.N) {
-            const float4 swn = *reinterpret_cast<const float4 *>(p.sw + n);
-            float t0 = ((float)acc[i][j][4 * g + 0] * sam) * swn.x;
-            float t1 = ((float)acc[i][j][4 * g + 1] * sam) * swn.y;
-            float t2 = ((float)acc[i][j][4 * g + 2] * sam) * swn.z;
-            float t3 = ((float)acc[i][j][4 * g + 3] * sam) * swn.w;
-            if (has_bias) {
-              const uint2 b = *reinterpret_cast<const uint2 *>(p.bias + n);
-              t0 = t0 + bf16_to_f32(b.x & 0xFFFFu);
-              t1 = t1 + bf16_to_f32(b.x >> 16);
-              t2 = t2 + bf16_to_f32(b.y & 0xFFFFu);
-              t3 = t3 + bf16_to_f32(b.y >> 16);
-            }
-            v.x = pack_bf16x2(t0, t1);
-            v.y = pack_bf16x2(t2, t3);
+          const float4 swn = *reinterpret_cast<const float4 *>(p.sw + n);
+          // without bias, adding -0 leaves every value (and its sign) as is
+          float4 bv = make_float4(-0.0f, -0.0f, -0.0f, -0.0f);
+          if (p.bias) {
+            const uint2 b = *reinterpret_cast<const uint2 *>(p.bias + n);
+            bv = make_float4(bf16_to_f32(b.x & 0xFFFFu), bf16_to_f32(b.x >> 16),
+                             bf16_to_f32(b.y & 0xFFFFu), bf16_to_f32(b.y >> 16));
           }
           const int c = nl >> 3, h = (nl >> 2) & 1;
-          const int off = r * ROWB + ((c ^ (r & (CPRW - 1))) << 4) +
-                          ((h ^ ((r >> 4) & 1)) << 3);
-          *reinterpret_cast<uint2 *>(region + off) = v;
+#pragma unroll
+          for (int j = 0; j < C::TM; ++j) {
+            const float t0 = ((float)acc[i][j][4 * g + 0] * sam[j]) * swn.x + bv.x;
+            const float t1 = ((float)acc[i][j][4 * g + 1] * sam[j]) * swn.y + bv.y;
+            const float t2 = ((float)acc[i][j][4 * g + 2] * sam[j]) * swn.z + bv.z;
+            const float t3 = ((float)acc[i][j][4 * g + 3] * sam[j]) * swn.w + bv.w;
+            const int r = j * 32 + (lane & 31);
+            const int off = r * ROWB + ((c ^ (r & (CPRW - 1))) << 4) +
+                            ((h ^ ((r >> 4) & 1)) << 3);
+            *reinterpret_cast<uint2 *>(region + off) =
+                make_uint2(pack_bf16x2(t0, t1), pack_bf16x2(t2, t3));
+          }
         }
       }
     }
