@@ -385,7 +385,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(KernelArgs p) {
     const int nb = n0 + wave_n * C::WN;
     // N is a multiple of 128 and so is nb: a wave's 128 channels are all
     // inside N or all past it (then nothing of this wave is stored).
-    if (nb < p.N) {
+    // Two copies of the arithmetic, with and without the bias add, so that
+    // neither carries a per-channel test.
+    auto stage_rows = [&](auto with_bias) {
+      constexpr bool kBias = decltype(with_bias)::value;
       float sam[C::TM];
 #pragma unroll
       for (int j = 0; j < C::TM; ++j) {
@@ -399,9 +402,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(KernelArgs p) {
           const int nl = i * 32 + 8 * g + 4 * (lane >> 5);
           const int n = nb + nl;
           const float4 swn = *reinterpret_cast<const float4 *>(p.sw + n);
-          // without bias, adding -0 leaves every value (and its sign) as is
-          float4 bv = make_float4(-0.0f, -0.0f, -0.0f, -0.0f);
-          if (p.bias) {
+          float4 bv;
+          if constexpr (kBias) {
             const uint2 b = *reinterpret_cast<const uint2 *>(p.bias + n);
             bv = make_float4(bf16_to_f32(b.x & 0xFFFFu), bf16_to_f32(b.x >> 16),
                              bf16_to_f32(b.y & 0xFFFFu), bf16_to_f32(b.y >> 16));
@@ -409,10 +411,16 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(KernelArgs p) {
           const int c = nl >> 3, h = (nl >> 2) & 1;
 #pragma unroll
           for (int j = 0; j < C::TM; ++j) {
-            const float t0 = ((float)acc[i][j][4 * g + 0] * sam[j]) * swn.x + bv.x;
-            const float t1 = ((float)acc[i][j][4 * g + 1] * sam[j]) * swn.y + bv.y;
-            const float t2 = ((float)acc[i][j][4 * g + 2] * sam[j]) * swn.z + bv.z;
-            const float t3 = ((float)acc[i][j][4 * g + 3] * sam[j]) * swn.w + bv.w;
+            float t0 = ((float)acc[i][j][4 * g + 0] * sam[j]) * swn.x;
+            float t1 = ((float)acc[i][j][4 * g + 1] * sam[j]) * swn.y;
+            float t2 = ((float)acc[i][j][4 * g + 2] * sam[j]) * swn.z;
+            float t3 = ((float)acc[i][j][4 * g + 3] * sam[j]) * swn.w;
+            if constexpr (kBias) {
+              t0 = t0 + bv.x;
+              t1 = t1 + bv.y;
+              t2 = t2 + bv.z;
+              t3 = t3 + bv.w;
+            }
             const int r = j * 32 + (lane & 31);
             const int off = r * ROWB + ((c ^ (r & (CPRW - 1))) << 4) +
                             ((h ^ ((r >> 4) & 1)) << 3);
@@ -421,6 +429,12 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(KernelArgs p) {
           }
         }
       }
+    };
+    if (nb < p.N) {
+      if (p.bias)
+        stage_rows(std::true_type{});
+      else
+        stage_rows(std::false_type{});
     }
     uint16_t *out = static_cast<uint16_t *>(p.out);
 #pragma unroll 4
