@@ -73,7 +73,8 @@ typedef enum {
  * in binary32 and rounded to the nearest integer, ties to even, clamped to
  * [-127, 127].  A row of zeros gives a_scale = 0 and zero codes.  FP32
  * subnormals are kept.
- * Shape: 1 <= M < 2^31, 8 <= K <= 90112 and K % 8 == 0 (16-byte rows of
+ * Shape: 1 <= M <= 2^24 - 1 (a launch holds fewer than 2^32 work-items,
+ * up to 256 per row), 8 <= K <= 90112 and K % 8 == 0 (16-byte rows of
  * BF16; a row stays in registers, 44 chunks per lane); rows whose
  * length is not a multiple of the kernel's chunk width are handled by
  * masking the partial chunk, as the LightX2V page's quantizer does
@@ -104,7 +105,10 @@ int w8a8_quantize_act(const uint16_t *x, int64_t M, int64_t K, int8_t *a_q,
  * follows "MLX implementation and experiment report" (MiniMax-H3-Image-mlx),
  * "What the default preserves".
  * Shape: 1 <= M < 2^31; N and K positive multiples of 128 (the LightX2V
- * page's shape contract, commit notes); N < 2^31; K <= W8A8_MAX_K.
+ * page's shape contract, commit notes); N < 2^31; K <= W8A8_MAX_K; and the
+ * tile grid (256 x 256 tiles of 512 work-items, or 64 x 128 tiles of 256)
+ * below 2^32 work-items: M * N up to about 2^39 (M <= 25.6 million at
+ * N = 21504).
  * Errors: NULL, SHAPE, ALIGN, WORKSPACE, OUT_DTYPE, ALIAS, DEVICE, HIP.
  */
 int w8a8_gemm(const int8_t *a_q, const float *a_scale, const int8_t *w_q,
@@ -118,7 +122,8 @@ int w8a8_gemm(const int8_t *a_q, const float *a_scale, const int8_t *w_q,
  *   x   BF16 [M,K] (16-byte aligned); y BF16 [M,N] (16-byte aligned);
  *   the other arguments as for w8a8_gemm.
  * Workspace: at least w8a8_linear_workspace_bytes(M, N, K) bytes, 256-byte
- * aligned, not overlapping any argument.  K <= 90112 (the quantizer's bound).
+ * aligned, not overlapping any argument.  K <= 90112 and M <= 2^24 - 1 (the
+ * quantizer's bounds).
  * Errors: as w8a8_gemm.
  */
 int w8a8_linear(const uint16_t *x, const int8_t *w_q, const float *w_scale,

@@ -87,6 +87,8 @@ def linear(**kw):
     (dict(M=0), SHAPE), (dict(M=-5), SHAPE), (dict(N=0), SHAPE),
     (dict(N=100), SHAPE), (dict(N=5376 + 64), SHAPE), (dict(K=5376 + 8), SHAPE),
     (dict(K=0), SHAPE), (dict(K=B.MAX_K + 128), SHAPE), (dict(M=1 << 31), SHAPE),
+    # tile grid beyond 2^32 work-items: 8388608 x 84 tiles of 512
+    (dict(M=(1 << 31) - 1, N=21504, wsb=1 << 62), SHAPE),
     (dict(dt=3), OUT_DTYPE), (dict(dt=-1), OUT_DTYPE),
     (dict(aq=BUF["aq"] + 8), ALIGN), (dict(w=BUF["w"] + 4), ALIGN),
     (dict(out=BUF["out"] + 2), ALIGN), (dict(sw=BUF["sw"] + 4), ALIGN),
@@ -129,7 +131,8 @@ def test_workspace_sizes():
 
 @pytest.mark.parametrize("kw,code", [
     (dict(x=None), NULL), (dict(q=None), NULL), (dict(s=None), NULL),
-    (dict(M=0), SHAPE), (dict(K=4), SHAPE), (dict(K=5377), SHAPE),
+    (dict(M=0), SHAPE), (dict(M=1 << 24), SHAPE),
+    (dict(K=4), SHAPE), (dict(K=5377), SHAPE),
     (dict(K=B.QUANT_MAX_K + 8), SHAPE),
     (dict(x=BUF["x"] + 8), ALIGN), (dict(q=BUF["aq"] + 4), ALIGN),
     (dict(s=BUF["sa"] + 1), ALIGN),

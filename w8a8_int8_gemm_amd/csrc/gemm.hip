@@ -810,6 +810,16 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   return plan;
 }
 
+bool plan_launchable(const GemmPlan &plan) {
+  // A launch holds fewer than 2^32 work-items per grid dimension.
+  const uint64_t lim = 0xFFFFFFFFull;
+  const uint64_t threads = plan.config == kCfgLarge ? CfgLarge::THREADS
+                                                     : CfgSkinny::THREADS;
+  if ((uint64_t)plan.main_tiles * threads > lim) return false;
+  if ((uint64_t)plan.tail_tiles * threads > lim) return false;
+  return (uint64_t)plan.tail_tiles * (CfgLarge::BM * CfgLarge::BN / 4) <= lim;
+}
+
 hipError_t launch_gemm(const GemmArgs &args, const GemmPlan &plan,
                        hipStream_t stream) {
   if (plan.config == kCfgLarge) return launch_cfg<CfgLarge>(args, plan, stream);

@@ -132,6 +132,8 @@ struct GemmPlan {
 };
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
+// Whether every launch of the plan fits the hardware grid limits.
+bool plan_launchable(const GemmPlan &plan);
 hipError_t launch_gemm(const GemmArgs &args, const GemmPlan &plan,
                        hipStream_t stream);
 

@@ -23,6 +23,9 @@ using w8a8::GemmPlan;
 // BF16 per lane x 4 waves x 64 lanes).
 constexpr int64_t kQuantMaxK = 44 * 8 * 4 * 64;
 constexpr int64_t kMaxRows = 0x7FFFFFFF;
+// Rows of the per-token kernels: their launches hold up to 256 work-items
+// per row, and a launch holds fewer than 2^32 work-items.
+constexpr int64_t kMaxTokenRows = (int64_t(1) << 24) - 1;
 
 thread_local int g_last_hip_error = 0;
 
@@ -77,7 +80,7 @@ bool gemm_shape_ok(int64_t M, int64_t N, int64_t K) {
 int validate_quant(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
                    const float *sa) {
   if (!x || !q || !sa) return W8A8_ERR_NULL;
-  if (M < 1 || M > kMaxRows || K < 8 || K % 8 != 0 || K > kQuantMaxK)
+  if (M < 1 || M > kMaxTokenRows || K < 8 || K % 8 != 0 || K > kQuantMaxK)
     return W8A8_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(q, 8) || !aligned(sa, 4))
     return W8A8_ERR_ALIGN;
@@ -111,6 +114,7 @@ int validate_gemm(const int8_t *a_q, const float *a_scale, const int8_t *w_q,
       (bias && !aligned(bias, 8)))
     return W8A8_ERR_ALIGN;
   *plan = w8a8::plan_gemm(M, N, K);
+  if (!w8a8::plan_launchable(*plan)) return W8A8_ERR_SHAPE;
   if (plan->workspace > 0) {
     if (!workspace || workspace_bytes < plan->workspace)
       return W8A8_ERR_WORKSPACE;
@@ -201,7 +205,8 @@ int w8a8_linear(const uint16_t *x, const int8_t *w_q, const float *w_scale,
                 int64_t K, void *workspace, size_t workspace_bytes,
                 void *stream) {
   if (!x || !w_q || !w_scale || !y) return W8A8_ERR_NULL;
-  if (!gemm_shape_ok(M, N, K) || K > kQuantMaxK) return W8A8_ERR_SHAPE;
+  if (!gemm_shape_ok(M, N, K) || K > kQuantMaxK || M > kMaxTokenRows)
+    return W8A8_ERR_SHAPE;
   if (!aligned(x, 16)) return W8A8_ERR_ALIGN;
   const size_t need = w8a8_linear_workspace_bytes(M, N, K);
   if (!workspace || workspace_bytes < need) return W8A8_ERR_WORKSPACE;
@@ -259,7 +264,7 @@ int w8a8_check_scales(const float *w_scale, int64_t N, int32_t *bad_count,
 int w8a8_swiglu_bf16(const uint16_t *h, uint16_t *y, int64_t M, int64_t F,
                      void *stream) {
   if (!h || !y) return W8A8_ERR_NULL;
-  if (M < 1 || M > kMaxRows || F < 8 || F % 8 != 0 || F > kMaxRows / 2)
+  if (M < 1 || M > kMaxTokenRows || F < 8 || F % 8 != 0 || F > kMaxRows / 2)
     return W8A8_ERR_SHAPE;
   if (!aligned(h, 16) || !aligned(y, 16)) return W8A8_ERR_ALIGN;
   if (overlap(range_of(h, M * F * 4), range_of(y, M * F * 2)))
@@ -273,7 +278,7 @@ int w8a8_swiglu_bf16(const uint16_t *h, uint16_t *y, int64_t M, int64_t F,
 int w8a8_quantize_act_swiglu(const uint16_t *h, int64_t M, int64_t F,
                              int8_t *a_q, float *a_scale, void *stream) {
   if (!h || !a_q || !a_scale) return W8A8_ERR_NULL;
-  if (M < 1 || M > kMaxRows || F < 8 || F % 8 != 0 || F > kQuantMaxK)
+  if (M < 1 || M > kMaxTokenRows || F < 8 || F % 8 != 0 || F > kQuantMaxK)
     return W8A8_ERR_SHAPE;
   if (!aligned(h, 16) || !aligned(a_q, 8) || !aligned(a_scale, 4))
     return W8A8_ERR_ALIGN;
@@ -302,7 +307,7 @@ int w8a8_silu_bf16(const uint16_t *x, uint16_t *y, int64_t n, void *stream) {
 int w8a8_pow2_renorm(const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                      void *stream) {
   if (!x || !y) return W8A8_ERR_NULL;
-  if (M < 1 || M > kMaxRows || K < 8 || K % 8 != 0 || K > kQuantMaxK)
+  if (M < 1 || M > kMaxTokenRows || K < 8 || K % 8 != 0 || K > kQuantMaxK)
     return W8A8_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(y, 16)) return W8A8_ERR_ALIGN;
   if (x != y && overlap(range_of(x, M * K * 2), range_of(y, M * K * 2)))
