@@ -211,3 +211,19 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(ImportError):
         B.lib()
+
+
+def test_binding_checks_tensors_before_calling():
+    """The wrappers check dtype, shape and device of every tensor before a
+    pointer reaches the C ABI (CPU tensors here: refused as not on a GPU)."""
+    import torch
+    a = torch.zeros((4, 128), dtype=torch.int8)
+    with pytest.raises(ValueError):
+        B.gemm(a, torch.zeros(4), torch.zeros((128, 128), dtype=torch.int8),
+               torch.zeros(128))
+    with pytest.raises(ValueError):
+        B.quantize_act(torch.zeros((4, 128), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        B.quantize_act(torch.zeros((4, 128), dtype=torch.float32))
+    with pytest.raises(TypeError):
+        B.pow2_renorm([[1.0]])

@@ -497,3 +497,24 @@ def test_gemm_epilogue_edge_values(orc):
         bad = np.argwhere(got != rb)
         assert bad.size == 0, (f"{len(bad)} differ, first "
                                f"{[(int(i), int(j), hex(got[i, j]), hex(rb[i, j])) for i, j in bad[:4]]}")
+
+
+def test_binding_rejects_mismatched_outputs():
+    # wrong output shapes or scale lengths never reach the C ABI
+    a = torch.zeros((64, 256), dtype=torch.int8, device="cuda")
+    w = torch.zeros((128, 256), dtype=torch.int8, device="cuda")
+    sa = torch.ones(64, device="cuda")
+    sw = torch.ones(128, device="cuda")
+    with pytest.raises(ValueError):
+        B.gemm(a, sa, w, sw, out=torch.empty((64, 64), dtype=torch.bfloat16,
+                                              device="cuda"))
+    with pytest.raises(ValueError):
+        B.gemm(a, sa[:32], w, sw)
+    with pytest.raises(ValueError):
+        B.gemm(a, sa, w, sw, out_dtype=torch.float32,
+               out=torch.empty((64, 128), dtype=torch.bfloat16, device="cuda"))
+    x = torch.zeros((8, 256), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        B.quantize_act(x, out=(torch.empty((8, 128), dtype=torch.int8,
+                                           device="cuda"),
+                               torch.empty(8, device="cuda")))

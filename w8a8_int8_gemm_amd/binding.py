@@ -102,15 +102,24 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _need(t, dtype, ndim, name):
+def _need(t, dtype, ndim, name, shape=None):
+    """t must be a contiguous tensor of `dtype` with `ndim` dims (and, if
+    given, exactly `shape`) on the current GPU: the C ABI takes bare
+    pointers, so sizes and devices are checked here."""
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype or t.dim() != ndim or not t.is_contiguous():
         raise ValueError(f"{name}: expected contiguous {dtype} with {ndim} "
                          f"dims, got {t.dtype} {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got "
+                         f"{tuple(t.shape)}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} must be on the current GPU "
+                         f"(cuda:{torch.cuda.current_device()})")
 
 
 def quantize_act(x, *, silu: bool = False, out=None, stream=None):
@@ -124,6 +133,8 @@ def quantize_act(x, *, silu: bool = False, out=None, stream=None):
         s = torch.empty((M,), dtype=torch.float32, device=x.device)
     else:
         q, s = out
+        _need(q, torch.int8, 2, "out[0]", (M, K))
+        _need(s, torch.float32, 1, "out[1]", (M,))
     fn = lib().w8a8_quantize_act_silu if silu else lib().w8a8_quantize_act
     _check("w8a8_quantize_act" + ("_silu" if silu else ""),
            fn(_ptr(x), M, K, _ptr(q), _ptr(s), _stream(stream)))
@@ -141,6 +152,8 @@ def linear_workspace_bytes(M: int, N: int, K: int) -> int:
 def _workspace(nbytes, device, given=None):
     torch = _torch()
     if given is not None:
+        if not given.is_contiguous() or not given.is_cuda:
+            raise ValueError("workspace must be a contiguous GPU tensor")
         return given
     if nbytes == 0:
         return None
@@ -159,17 +172,19 @@ def gemm(a_q, a_scale, w_q, w_scale, bias=None, out_dtype=None, *, out=None,
     if out_dtype not in codes:
         raise ValueError(f"out_dtype {out_dtype} not supported")
     _need(a_q, torch.int8, 2, "a_q")
-    _need(a_scale, torch.float32, 1, "a_scale")
-    _need(w_q, torch.int8, 2, "w_q")
-    _need(w_scale, torch.float32, 1, "w_scale")
-    if bias is not None:
-        _need(bias, torch.bfloat16, 1, "bias")
     M, K = a_q.shape
+    _need(w_q, torch.int8, 2, "w_q")
     N = w_q.shape[0]
     if w_q.shape[1] != K:
         raise ValueError("a_q and w_q disagree on K")
+    _need(a_scale, torch.float32, 1, "a_scale", (M,))
+    _need(w_scale, torch.float32, 1, "w_scale", (N,))
+    if bias is not None:
+        _need(bias, torch.bfloat16, 1, "bias", (N,))
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
+    else:
+        _need(out, out_dtype, 2, "out", (M, N))
     ws_need = workspace_bytes(M, N, K)
     ws = _workspace(ws_need, a_q.device, workspace)
     ws_len = 0 if ws is None else ws.numel() * ws.element_size()
@@ -185,14 +200,18 @@ def linear(x, w_q, w_scale, bias=None, *, out=None, workspace=None,
     """y = bf16(((float)(quant(x) . w_q^T) * sa) * sw + bias)."""
     torch = _torch()
     _need(x, torch.bfloat16, 2, "x")
-    _need(w_q, torch.int8, 2, "w_q")
-    _need(w_scale, torch.float32, 1, "w_scale")
-    if bias is not None:
-        _need(bias, torch.bfloat16, 1, "bias")
     M, K = x.shape
+    _need(w_q, torch.int8, 2, "w_q")
     N = w_q.shape[0]
+    if w_q.shape[1] != K:
+        raise ValueError("x and w_q disagree on K")
+    _need(w_scale, torch.float32, 1, "w_scale", (N,))
+    if bias is not None:
+        _need(bias, torch.bfloat16, 1, "bias", (N,))
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _need(out, torch.bfloat16, 2, "out", (M, N))
     ws = _workspace(linear_workspace_bytes(M, N, K), x.device, workspace)
     ws_len = 0 if ws is None else ws.numel() * ws.element_size()
     _check("w8a8_linear", lib().w8a8_linear(
@@ -203,9 +222,9 @@ def linear(x, w_q, w_scale, bias=None, *, out=None, workspace=None,
 
 def silu(x, *, out=None, stream=None):
     torch = _torch()
-    if x.dtype != torch.bfloat16 or not x.is_contiguous() or not x.is_cuda:
-        raise ValueError("x must be a contiguous bf16 GPU tensor")
+    _need(x, torch.bfloat16, x.dim(), "x")
     y = torch.empty_like(x) if out is None else out
+    _need(y, torch.bfloat16, x.dim(), "out", tuple(x.shape))
     _check("w8a8_silu_bf16", lib().w8a8_silu_bf16(
         _ptr(x), _ptr(y), x.numel(), _stream(stream)))
     return y
@@ -216,6 +235,7 @@ def pow2_renorm(x, *, out=None, stream=None):
     _need(x, torch.bfloat16, 2, "x")
     M, K = x.shape
     y = torch.empty_like(x) if out is None else out
+    _need(y, torch.bfloat16, 2, "out", (M, K))
     _check("w8a8_pow2_renorm", lib().w8a8_pow2_renorm(
         _ptr(x), _ptr(y), M, K, _stream(stream)))
     return y
@@ -232,6 +252,8 @@ def quantize_weight(w, *, out=None, stream=None):
         s = torch.empty((N,), dtype=torch.float32, device=w.device)
     else:
         q, s = out
+        _need(q, torch.int8, 2, "out[0]", (N, K))
+        _need(s, torch.float32, 1, "out[1]", (N,))
     _check("w8a8_quantize_weight", lib().w8a8_quantize_weight(
         _ptr(w), N, K, _ptr(q), _ptr(s), _stream(stream)))
     return q, s
@@ -243,6 +265,7 @@ def check_scales(w_scale, *, out=None, stream=None):
     _need(w_scale, torch.float32, 1, "w_scale")
     bad = (torch.empty((1,), dtype=torch.int32, device=w_scale.device)
            if out is None else out)
+    _need(bad, torch.int32, 1, "out", (1,))
     _check("w8a8_check_scales", lib().w8a8_check_scales(
         _ptr(w_scale), w_scale.numel(), _ptr(bad), _stream(stream)))
     return bad
@@ -257,6 +280,7 @@ def swiglu(h, *, out=None, stream=None):
         raise ValueError("h must have an even width (gate | up)")
     y = (torch.empty((M, F2 // 2), dtype=torch.bfloat16, device=h.device)
          if out is None else out)
+    _need(y, torch.bfloat16, 2, "out", (M, F2 // 2))
     _check("w8a8_swiglu_bf16", lib().w8a8_swiglu_bf16(
         _ptr(h), _ptr(y), M, F2 // 2, _stream(stream)))
     return y
@@ -275,6 +299,8 @@ def quantize_act_swiglu(h, *, out=None, stream=None):
         s = torch.empty((M,), dtype=torch.float32, device=h.device)
     else:
         q, s = out
+        _need(q, torch.int8, 2, "out[0]", (M, F2 // 2))
+        _need(s, torch.float32, 1, "out[1]", (M,))
     _check("w8a8_quantize_act_swiglu", lib().w8a8_quantize_act_swiglu(
         _ptr(h), M, F2 // 2, _ptr(q), _ptr(s), _stream(stream)))
     return q, s
