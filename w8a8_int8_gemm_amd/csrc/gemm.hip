@@ -765,6 +765,12 @@ constexpr int kCUs = 256;
 #ifndef W8A8_GROUP_M_WIDE
 #define W8A8_GROUP_M_WIDE 4
 #endif
+#ifndef W8A8_SKINNY_WGS_PER_CU
+#define W8A8_SKINNY_WGS_PER_CU 1
+#endif
+#ifndef W8A8_SKINNY_MIN_STAGES
+#define W8A8_SKINNY_MIN_STAGES 8
+#endif
 // Fewest K slices that make a split tail launch worthwhile.
 #ifndef W8A8_TAIL_MIN_SPLITS
 #define W8A8_TAIL_MIN_SPLITS 2
@@ -795,17 +801,19 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     }
     return plan;
   }
-  // Few tiles: smaller tiles, and split K while the grid is under one wave
-  // of the chip and each slice keeps at least 8 stages.
+  // Few tiles: smaller tiles, and split K so that about
+  // W8A8_SKINNY_WGS_PER_CU work groups per CU stream the weights, each
+  // slice keeping at least W8A8_SKINNY_MIN_STAGES stages.
   plan.config = kCfgSkinny;
   plan.group_m = CfgSkinny::GROUP_M;
   const int64_t tiles =
       ((M + CfgSkinny::BM - 1) / CfgSkinny::BM) * ((N + CfgSkinny::BN - 1) / CfgSkinny::BN);
   plan.main_tiles = (int)tiles;
   const int64_t stages = K / CfgSkinny::BK;
-  int splits = 1;
-  while (tiles * splits * 2 <= kCUs && stages / (splits * 2) >= 8) splits *= 2;
-  plan.splits = splits;
+  const int64_t splits = std::max<int64_t>(
+      1, std::min<int64_t>(kCUs * W8A8_SKINNY_WGS_PER_CU / tiles,
+                           stages / W8A8_SKINNY_MIN_STAGES));
+  plan.splits = (int)splits;
   plan.workspace = splits > 1 ? (size_t)(splits * M * N * sizeof(int32_t)) : 0;
   return plan;
 }
