@@ -90,9 +90,9 @@ def main():
         traffic_calibration()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the projection shards by tokens with no exchange; see the "
-              "design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(the projection would shard by tokens with no exchange). "
+              "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
