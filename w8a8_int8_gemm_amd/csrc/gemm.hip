@@ -364,6 +364,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(KernelArgs p) {
     for (int kt = 0; kt + 1 < nk; ++kt) stage(kt, false);
     stage(nk - 1, true);
   }
+  // The drain copies may still be landing in LDS: they must have landed
+  // before the epilogue reuses the ring or the work group releases it.
+  wait_vmcnt<0>();
 
   // Epilogue.  Lane holds token m = base + (lane & 31) and, for register
   // 4g + t, channel n = base + 8g + 4*(lane >> 5) + t.
@@ -378,8 +381,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(KernelArgs p) {
     constexpr int ROWB = C::WN * 2;    // bytes per staged row
     constexpr int CPRW = ROWB / 16;    // 16-byte chunks per staged row
     constexpr int RPI = 64 / CPRW;     // staged rows per wave read
-    wait_vmcnt<0>();  // every direct load, including drain copies, landed
-    block_barrier();  // and every wave is done reading the ring
+    block_barrier();  // every wave is done reading the ring
     int8_t *region = smem + wave * (C::WM * ROWB);
     const int mb = m0 + wave_m * C::WM;
     const int nb = n0 + wave_n * C::WN;
