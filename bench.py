@@ -38,6 +38,8 @@ ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
 INT8_PEAK_TOPS = 5000.0   # MI355X dense INT8 MFMA, published
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
+GRAPH_GEMM_REPEATS = 20   # GEMM calls per timing graph (single projection)
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 MFMA, published
 METRIC = ("W8A8 projection TOPS and % INT8 MFMA peak at DiT shapes "
           "(M~19k, K=5376)")
@@ -61,6 +63,11 @@ def parse():
     ap.add_argument("--fused-qkv", action="store_true",
                     help="run Q, K and V as one GEMM over the concatenated "
                          "weights [3N, K] (same outputs, bit for bit)")
+    ap.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
+                    help="replay the step (and the GEMM-only timing) as a "
+                         "HIP graph; auto = on for the single-projection "
+                         "workload, whose kernels are shorter than the "
+                         "Python launch path")
     ap.add_argument("--traffic-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 4 times (a kernel "
                          "of known HBM traffic for scaling rocprofv3's "
@@ -201,6 +208,22 @@ def main():
         step(False)
     torch.cuda.synchronize()
 
+    # Graph mode: one step captured once and replayed; the library records
+    # kernel launches only (no memsets, no host synchronization).
+    use_graph = args.graph == "on" or (args.graph == "auto" and single)
+    if use_graph:
+        step_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(step_graph):
+            graph_out = step(False)
+        torch.cuda.synchronize()
+
+        def run_step():
+            step_graph.replay()
+            return graph_out
+    else:
+        def run_step():
+            return step(False)
+
     # Timed region 1: the steps alone (value).  An event recorded between
     # two kernels costs a few microseconds of queue time, so the per-call
     # GEMM events are kept out of this region.
@@ -209,30 +232,61 @@ def main():
     torch.cuda.synchronize()
     start.record()
     for _ in range(args.steps):
-        out = step(False)
+        out = run_step()
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / max(args.steps, 1)
     tops = ops_per_step / (ms_per_step * 1e-3) / 1e12
 
-    # Timed region 2: the same steps with HIP events around every GEMM call
-    # on the launch stream (roofline: average duration of one call).
-    all_gemm = []
-    torch.cuda.synchronize()
-    for _ in range(args.steps):
-        out = step(True)
-        all_gemm.append(gemm_events)
-    torch.cuda.synchronize()
-
-    # per-launch GEMM durations
+    # Timed region 2 (roofline: average duration of one GEMM call).  Eager:
+    # the same steps with HIP events around every GEMM call on the launch
+    # stream.  Graph mode: a graph of the step's GEMM calls alone (on the
+    # buffers the step filled), replayed between two events.
     gemm_ms = 0.0
     launches = 0
-    for evs in all_gemm:
-        for i in range(0, len(evs), 2):
-            gemm_ms += evs[i].elapsed_time(evs[i + 1])
-            launches += 1
-    gemm_ops = ops_per_step * args.steps
+    torch.cuda.synchronize()
+    if use_graph:
+        calls = []
+
+        def gemm_call(name, phase):
+            if phase == "begin":
+                calls.append(name)
+        gemm_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gemm_graph):
+            if single:
+                p = blocks[0][wl.projs[0].name]
+                for _ in range(GRAPH_GEMM_REPEATS):
+                    B.gemm(qbuf, sbuf, p.w, p.sw, p.bias, out=ybuf,
+                           workspace=wsb)
+                    calls.append(p.name)
+            else:
+                for blk in blocks:
+                    runner.run_gemms(blk, on_gemm=gemm_call)
+        gemm_graph.replay()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(args.steps):
+            gemm_graph.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        gemm_ms = ev0.elapsed_time(ev1)
+        launches = len(calls) * args.steps
+        gemm_ops = args.steps * sum(
+            2 * M * blocks[0][n].N * blocks[0][n].K for n in calls)
+    else:
+        all_gemm = []
+        for _ in range(args.steps):
+            out = step(True)
+            all_gemm.append(gemm_events)
+        torch.cuda.synchronize()
+        for evs in all_gemm:
+            for i in range(0, len(evs), 2):
+                gemm_ms += evs[i].elapsed_time(evs[i + 1])
+                launches += 1
+        gemm_ops = ops_per_step * args.steps
     gemm_tops = gemm_ops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None
     avg_launch_us = gemm_ms * 1e3 / max(launches, 1)
     log(f"[bench] step {ms_per_step:.3f} ms -> {tops:.1f} TOPS "
@@ -289,19 +343,9 @@ def main():
             "parallelism": "single_gpu",
         },
         "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
-        "roofline": {
-            "kernel": ("w8a8_gemm call: gemm_kernel (INT8 MFMA + fused "
-                       "epilogue), plus its split-K tail launch and tail "
-                       "reduction where the last wave of tiles is short"),
-            "bound": "mfma",
-            "achieved": round(gemm_tops, 2) if gemm_tops else None,
-            "peak": INT8_PEAK_TOPS,
-            "unit": "TOP/s",
-            "frac": round(gemm_tops / INT8_PEAK_TOPS, 4) if gemm_tops else None,
-            "avg_launch_us": round(avg_launch_us, 2),
-            "launches_timed": launches,
-            "traffic": traffic_entry(),
-        },
+        "roofline": roofline_entry(blocks[0], M, gemm_tops, avg_launch_us,
+                                   launches, use_graph,
+                                   traffic_entry(wl, args.fused_qkv)),
         "cpu_baseline": cpu,
         "bf16_baseline": bf16,
         "oracle_check": check,
@@ -309,15 +353,62 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def traffic_entry():
+def gemm_call_bytes(M, N, K):
+    """Algorithmic HBM bytes of one w8a8_gemm call: A and W read once, the
+    BF16 output written once, the FP32 scales and the BF16 bias read."""
+    return M * K + N * K + 2 * M * N + 4 * M + 4 * N + 2 * N
+
+
+def roofline_entry(blk, M, gemm_tops, avg_launch_us, launches, graph,
+                   traffic):
+    """Roofline of the dominant kernel (one w8a8_gemm call).  A workload
+    whose calls average fewer ops per byte than the chip's ridge point
+    (5.0 POPS / 8 TB/s = 625) is bounded by HBM and reported in GB/s."""
+    shapes = [(p.N, p.K) for p in blk.values()]
+    ops = sum(2 * M * N * K for N, K in shapes) / len(shapes)
+    nbytes = sum(gemm_call_bytes(M, N, K) for N, K in shapes) / len(shapes)
+    hbm = ops / nbytes < INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if hbm:
+        achieved = nbytes / (avg_launch_us * 1e-6) / 1e9 if avg_launch_us \
+            else None
+        peak, unit = HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = gemm_tops, INT8_PEAK_TOPS, "TOP/s"
+    return {
+        "kernel": ("w8a8_gemm call: gemm_kernel (INT8 MFMA + fused "
+                   "epilogue), plus its split-K tail launch and tail "
+                   "reduction where the last wave of tiles is short, or "
+                   "its split-K reduction for skinny M"),
+        "bound": "hbm" if hbm else "mfma",
+        "achieved": round(achieved, 2) if achieved else None,
+        "peak": peak,
+        "unit": unit,
+        "frac": round(achieved / peak, 4) if achieved else None,
+        "algorithmic_bytes_per_call": int(nbytes),
+        "algorithmic_ops_per_call": int(ops),
+        "avg_launch_us": round(avg_launch_us, 2),
+        "launches_timed": launches,
+        "timing": ("graph of back-to-back calls between two HIP events"
+                   if graph else "HIP events around every call"),
+        "traffic": traffic,
+    }
+
+
+def traffic_entry(wl, fused_qkv):
     """Measured HBM bytes per GEMM launch from committed rocprofv3 counter
-    summaries, valid only while the kernel source is unchanged."""
-    import hashlib
+    summaries: valid only for the projection mix they were taken on (the
+    six calls of a block at its token count and shapes) and only while the
+    kernel source is unchanged."""
     f = ROOT / "profiles" / "gemm_traffic.json"
-    if not f.exists():
+    if not f.exists() or fused_qkv:
         return None
     rec = json.loads(f.read_text())
     if rec.get("kernel_sha256") != kernel_source_sha256():
+        return None
+    mix = rec.get("workload", {})
+    if (mix.get("tokens") != wl.M or
+            sorted(map(tuple, mix.get("shapes_NK", []))) !=
+            sorted((p.N, p.K) for p in wl.projs)):
         return None
     return rec.get("traffic")
 

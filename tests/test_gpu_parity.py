@@ -355,6 +355,59 @@ def test_gemm_tail_split(orc, M, N, K):
     assert np.array_equal(yb, rb)
 
 
+@pytest.mark.parametrize("M,N,K", [(64, 5376, 5376), (4097, 4096, 1024)])
+def test_graph_replay(orc, M, N, K):
+    # The library enqueues kernel launches only (no memsets, no host waits),
+    # so a HIP graph of quantize + GEMM + SiLU-quantize replays the eager
+    # results bit for bit.  M=64 takes the skinny split-K path and its
+    # reduction; 4097 x 4096 the tail split and tail reduction.  Outputs are
+    # overwritten with a pattern before every replay, and eager library
+    # calls on other buffers run between the replays.
+    say(f"graph replay M={M} N={N} K={K}")
+    x = D.activations(M, K, seed=7)
+    w, sw, b = D.weights(N, K, seed=7), D.weight_scales(N, seed=7), \
+        D.bias(N, seed=7)
+    xd, wd, swd, bd = dev_bf16(x), dev(w), dev(sw), dev_bf16(b)
+    q = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    s = torch.empty((M,), dtype=torch.float32, device="cuda")
+    hq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    hs = torch.empty((M,), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty((max(B.workspace_bytes(M, N, K), 256),),
+                     dtype=torch.uint8, device="cuda")
+
+    def enqueue():
+        B.quantize_act(xd, out=(q, s))
+        B.gemm(q, s, wd, swd, bd, out=y, workspace=ws)
+        B.quantize_act(xd, silu=True, out=(hq, hs))
+
+    outs = (q, s, y, hq, hs)
+    enqueue()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    rows = np.array([0, M // 2, M - 1])
+    assert np.array_equal(host_bf16(ref[2])[rows],
+                          orc.linear(x[rows], w, sw, b))
+
+    oa, ow, osa, osw, obias = gemm_inputs(300, 384, 1152, 9)
+    other_args = (dev(oa), dev(osa), dev(ow), dev(osw), dev_bf16(obias))
+    other = torch.empty((300, 384), dtype=torch.bfloat16, device="cuda")
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        enqueue()
+    for r in range(3):
+        for t in outs:
+            t.view(torch.uint8).fill_(0x5A)
+        graph.replay()
+        B.gemm(*other_args, out=other)
+        torch.cuda.synchronize()
+        for name, t, want in zip(("codes", "scales", "y", "silu codes",
+                                  "silu scales"), outs, ref):
+            assert torch.equal(t.view(torch.uint8), want.view(torch.uint8)), \
+                f"replay {r}: {name} differ from the eager call"
+
+
 @pytest.mark.parametrize("M", [300, 4096])
 def test_fused_qkv_equals_separate(orc, M):
     # one GEMM over [3N, K] (N = 16128 at the block's width) against the three

@@ -111,16 +111,30 @@ class BlockRunner:
         need.append(B.workspace_bytes(M, 3 * shape["q"][0], H))
         self.ws = e(max(max(need), 256), dt=torch.uint8)
 
+    def _gemm(self, projs, name, q, s, stream, on_gemm):
+        p = projs[name]
+        if on_gemm:
+            on_gemm(name, "begin")
+        B.gemm(q, s, p.w, p.sw, p.bias, out=self.out[name],
+               workspace=self.ws, stream=stream)
+        if on_gemm:
+            on_gemm(name, "end")
+
+    def run_gemms(self, projs: dict, stream=None, on_gemm=None):
+        """Only the block's GEMM calls, on the codes and scales the last
+        ``run`` left in the buffers (GEMM timing)."""
+        for n in (("qkv",) if "qkv" in projs else ("q", "k", "v")):
+            self._gemm(projs, n, self.xq[0], self.xs[0], stream, on_gemm)
+        self._gemm(projs, "o", self.oq if self.o_input == "v" else self.xq[1],
+                   self.xs[1], stream, on_gemm)
+        self._gemm(projs, "fc1", self.xq[2], self.xs[2], stream, on_gemm)
+        self._gemm(projs, "fc2", self.hq, self.hs, stream, on_gemm)
+        return self.out
+
     def run(self, x, projs: dict, stream=None, on_gemm=None):
         """x: bf16 [M, H].  Returns the dict of BF16 outputs."""
         def gemm(name, q, s):
-            p = projs[name]
-            if on_gemm:
-                on_gemm(name, "begin")
-            B.gemm(q, s, p.w, p.sw, p.bias, out=self.out[name],
-                   workspace=self.ws, stream=stream)
-            if on_gemm:
-                on_gemm(name, "end")
+            self._gemm(projs, name, q, s, stream, on_gemm)
 
         # Q, K, V: one shared quantization of the block input (and, fused,
         # one GEMM over the concatenated weights).
