@@ -112,16 +112,17 @@ def test_gemm_workspace_checks():
 
 def test_workspace_sizes():
     # 256x256 tiles: a full number of 256-tile waves needs no workspace; a
-    # short last wave (t tiles) is split s = min(256 // t, stages // 8) ways
-    # into INT32 tiles of its own when s >= 2.
+    # short last wave (t tiles) is split s = min(256 // t, K // 512) ways
+    # into INT32 tiles of its own when s >= 2 (each slice at least 512
+    # bytes of K, four 128-byte stages).
     tile = 256 * 256 * 4
     assert B.workspace_bytes(4096, 4096, 5376) == 0           # 256 tiles
     assert B.workspace_bytes(19077, 21504, 5376) == 0         # 6300: s = 1
     assert B.workspace_bytes(19077, 5376, 5376) == 6 * 39 * tile   # 1575
     assert B.workspace_bytes(37503, 5376, 21504) == 17 * 15 * tile  # 3087
-    assert B.workspace_bytes(4097, 4096, 1664) == 3 * 16 * tile    # 26 stages
+    assert B.workspace_bytes(4097, 4096, 1664) == 3 * 16 * tile    # 13 stages
     assert B.workspace_bytes(4097, 4096, 1024) == 2 * 16 * tile
-    assert B.workspace_bytes(4097, 4096, 512) == 0            # 8 stages
+    assert B.workspace_bytes(4097, 4096, 512) == 0            # 4 stages
     ws = B.workspace_bytes(64, 5376, 5376)
     assert ws % (64 * 5376 * 4) == 0 and ws // (64 * 5376 * 4) >= 2
     assert B.workspace_bytes(64, 100, 5376) == 0  # rejected shape

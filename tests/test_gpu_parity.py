@@ -249,6 +249,7 @@ def test_quantize_act_swiglu(orc, M, F):
 # ---------------------------------------------------------------------------
 
 GEMM_SHAPES = [(1, 128, 128), (3, 384, 256), (64, 5376, 5376),
+               (32, 128, 1280), (33, 384, 1152), (64, 256, 21504),
                (65, 256, 384), (257, 1280, 2048), (300, 384, 1152),
                (513, 768, 640), (1000, 640, 256)]
 
@@ -328,8 +329,9 @@ def test_linear(orc, M, N, K):
                                    (4396, 3968, 2048), (65541, 128, 1024)])
 def test_gemm_tail_split(orc, M, N, K):
     # 4097 x 4096: 17 x 16 tiles of 256 x 256: one full wave of 256 tiles,
-    # then the 16 tiles of the one-row last token tile split K (26 stages in
-    # 3 slices of 8/9/9, or 16 stages in 2) and summed by the tail reduction.
+    # then the 16 tiles of the one-row last token tile split K (13 stages of
+    # 128 bytes in 3 slices of 4/4/5, or 8 stages in 2) and summed by the
+    # tail reduction.
     # 4396 x 3968: 18 x 16 tiles whose last token tile holds 44 rows and last
     # channel tile 128 channels; 32 tail tiles in 4 slices.  65541 x 128:
     # one channel tile, half of it past N, 257 tiles, the last (5 rows)
