@@ -251,7 +251,11 @@ def test_quantize_act_swiglu(orc, M, F):
 GEMM_SHAPES = [(1, 128, 128), (3, 384, 256), (64, 5376, 5376),
                (32, 128, 1280), (33, 384, 1152), (64, 256, 21504),
                (65, 256, 384), (257, 1280, 2048), (300, 384, 1152),
-               (513, 768, 640), (1000, 640, 256)]
+               (513, 768, 640), (1000, 640, 256),
+               # a wave of 64x128 tiles, unsplit, 128-byte stages
+               (1100, 2048, 640),
+               # half a wave or more of 256x256 tiles (ragged M and N)
+               (2100, 3968, 384)]
 
 
 def gemm_inputs(M, N, K, seed):

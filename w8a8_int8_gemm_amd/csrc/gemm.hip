@@ -628,16 +628,22 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(
 // Large M: 256x256 tiles, 8 waves (two per SIMD) of 64x128, two slots of
 // 128-byte K stages (128 KiB LDS): each direct load then fills whole
 // 128-byte lines of 8 rows, where 64-byte stages used half lines of 16 rows
-// (5% faster on the DiT shapes).  Small M: 64x128 tiles, 4 waves of 64x32,
-// a 4-slot ring of 64-byte stages.
+// (5% faster on the DiT shapes).  Small M: 64x128 tiles, 4 waves of 64x32:
+// a 4-slot ring of 64-byte stages when few tiles split K (more stages in
+// flight per byte), two slots of 128-byte stages when the tiles fill the
+// chip unsplit.
 #ifndef W8A8_CFG_LARGE
 #define W8A8_CFG_LARGE 256, 256, 128, 4, 2, 4, 2
 #endif
 #ifndef W8A8_CFG_SKINNY
 #define W8A8_CFG_SKINNY 64, 128, 64, 1, 4, 1, 4
 #endif
+#ifndef W8A8_CFG_MID
+#define W8A8_CFG_MID 64, 128, 128, 1, 4, 1, 2
+#endif
 using CfgLarge = Cfg<W8A8_CFG_LARGE>;
 using CfgSkinny = Cfg<W8A8_CFG_SKINNY>;
+using CfgMid = Cfg<W8A8_CFG_MID>;
 
 template <class C>
 hipError_t set_lds_limit();
@@ -761,6 +767,7 @@ hipError_t set_lds_limit() {
 
 constexpr int kCfgLarge = 0;
 constexpr int kCfgSkinny = 1;
+constexpr int kCfgMid = 2;
 constexpr int kCUs = 256;
 
 // Token tiles per group of the tile order: a narrow output (few channel
@@ -784,6 +791,15 @@ constexpr int kCUs = 256;
 #endif
 #ifndef W8A8_TAIL_MIN_K
 #define W8A8_TAIL_MIN_K 512
+#endif
+// Fewer than a wave of 256x256 tiles still runs as one partial wave of
+// them when the 64x128 tiles would not all be resident at once (three work
+// groups per CU) or when there are at least this many large tiles: one
+// large-tile time then beats the small tiles (measured at N=5376, K=5376:
+// M=1280, 105 large tiles, 61 us against 81 us of small tiles; M=1024, 84
+// large tiles, small tiles win with 55 us).
+#ifndef W8A8_LARGE_MIN_TILES
+#define W8A8_LARGE_MIN_TILES 112
 #endif
 
 }  // namespace
@@ -812,13 +828,18 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     }
     return plan;
   }
+  const int64_t tiles =
+      ((M + CfgSkinny::BM - 1) / CfgSkinny::BM) * ((N + CfgSkinny::BN - 1) / CfgSkinny::BN);
+  constexpr int64_t kMidResident = (160 * 1024 / CfgMid::LDS) * kCUs;
+  if (large_tiles >= W8A8_LARGE_MIN_TILES || tiles > kMidResident) {
+    plan.main_tiles = (int)large_tiles;
+    return plan;
+  }
   // Few tiles: smaller tiles, and split K so that about
   // W8A8_SKINNY_WGS_PER_CU work groups per CU stream the weights, each
   // slice keeping at least W8A8_SKINNY_MIN_STAGES stages.
   plan.config = kCfgSkinny;
   plan.group_m = CfgSkinny::GROUP_M;
-  const int64_t tiles =
-      ((M + CfgSkinny::BM - 1) / CfgSkinny::BM) * ((N + CfgSkinny::BN - 1) / CfgSkinny::BN);
   plan.main_tiles = (int)tiles;
   const int64_t stages = K / CfgSkinny::BK;
   const int64_t splits = std::max<int64_t>(
@@ -826,14 +847,21 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
                            stages / W8A8_SKINNY_MIN_STAGES));
   plan.splits = (int)splits;
   plan.workspace = splits > 1 ? (size_t)(splits * M * N * sizeof(int32_t)) : 0;
+  // A wave or more of small tiles: no split, and 128-byte stages.
+  if (splits == 1 && tiles >= kCUs) {
+    static_assert(CfgMid::BM == CfgSkinny::BM && CfgMid::BN == CfgSkinny::BN,
+                  "same tiles");
+    plan.config = kCfgMid;
+  }
   return plan;
 }
 
 bool plan_launchable(const GemmPlan &plan) {
   // A launch holds fewer than 2^32 work-items per grid dimension.
   const uint64_t lim = 0xFFFFFFFFull;
-  const uint64_t threads = plan.config == kCfgLarge ? CfgLarge::THREADS
-                                                     : CfgSkinny::THREADS;
+  const uint64_t threads = plan.config == kCfgLarge  ? CfgLarge::THREADS
+                           : plan.config == kCfgMid ? CfgMid::THREADS
+                                                    : CfgSkinny::THREADS;
   if ((uint64_t)plan.main_tiles * threads > lim) return false;
   if ((uint64_t)plan.tail_tiles * threads > lim) return false;
   return (uint64_t)plan.tail_tiles * (CfgLarge::BM * CfgLarge::BN / 4) <= lim;
@@ -842,6 +870,7 @@ bool plan_launchable(const GemmPlan &plan) {
 hipError_t launch_gemm(const GemmArgs &args, const GemmPlan &plan,
                        hipStream_t stream) {
   if (plan.config == kCfgLarge) return launch_cfg<CfgLarge>(args, plan, stream);
+  if (plan.config == kCfgMid) return launch_cfg<CfgMid>(args, plan, stream);
   return launch_cfg<CfgSkinny>(args, plan, stream);
 }
 
