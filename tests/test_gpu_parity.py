@@ -329,6 +329,37 @@ def test_linear(orc, M, N, K):
     assert np.array_equal(y, orc.linear(x, w, sw, b))
 
 
+@pytest.mark.parametrize("M,N", [(3, 256), (300, 512), (1100, 2048),
+                                 (4097, 4096)])
+def test_gemm_max_k_closed_form(M, N):
+    # K at the INT32 bound: A[m, k] = a_m and W[n, k] = w_n with a_m, w_n
+    # drawn from {-128, -127, -1, 0, 1, 127}, so acc[m, n] = a_m * w_n * K
+    # exactly, up to 128 * 128 * 130944 = 2145386496 < 2^31.  Covers the
+    # split-K slices (M = 3, 300), the unsplit small tiles (1100) and the
+    # large tiles with a split tail (4097) over the longest K.
+    K = B.MAX_K
+    g = np.random.default_rng([11, M, N])
+    vals = np.array([-128, -127, -1, 0, 1, 127], np.int64)
+    am = vals[g.integers(0, len(vals), M)]
+    wn = vals[g.integers(0, len(vals), N)]
+    am[0], wn[0] = -128, -128   # the largest positive accumulator
+    say(f"gemm max K M={M} N={N} K={K} workspace={B.workspace_bytes(M, N, K)}")
+    a = torch.from_numpy(am.astype(np.int8)).cuda()[:, None].expand(M, K) \
+        .contiguous()
+    w = torch.from_numpy(wn.astype(np.int8)).cuda()[:, None].expand(N, K) \
+        .contiguous()
+    ones_m = torch.ones(M, dtype=torch.float32, device="cuda")
+    ones_n = torch.ones(N, dtype=torch.float32, device="cuda")
+    out = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    B.gemm(a, ones_m, w, ones_n, None, out_dtype=torch.int32, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.int64)
+    want = np.outer(am, wn) * K
+    assert want.max() == 128 * 128 * K < 2 ** 31
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} accumulators differ: {bad[:5].tolist()}"
+
+
 @pytest.mark.parametrize("M,N,K", [(4097, 4096, 1664), (4097, 4096, 1024),
                                    (4396, 3968, 2048), (65541, 128, 1024)])
 def test_gemm_tail_split(orc, M, N, K):
