@@ -329,6 +329,38 @@ def test_linear(orc, M, N, K):
     assert np.array_equal(y, orc.linear(x, w, sw, b))
 
 
+# Seeded random shapes, two or more for each of the planner's paths (found
+# by drawing M < 9000, N and K multiples of 128 and classifying them with
+# the plan rules): one partial wave of 256x256 tiles, unsplit 64x128 tiles
+# with 128-byte stages, 64x128 tiles with 64-byte stages (unsplit and
+# split-K), and whole waves of 256x256 tiles.
+RANDOM_SHAPES = [(3024, 3456, 640), (7666, 1152, 128), (1415, 1792, 512),
+                 (825, 2688, 896), (887, 1920, 512), (706, 1664, 384),
+                 (38, 2048, 1280), (17, 256, 2560), (5968, 5120, 128)]
+
+
+@pytest.mark.parametrize("M,N,K", RANDOM_SHAPES)
+def test_gemm_random_shapes(orc, M, N, K):
+    say(f"gemm random shape M={M} N={N} K={K} "
+        f"workspace={B.workspace_bytes(M, N, K)}")
+    a, w, sa, sw, bias = gemm_inputs(M, N, K, 12)
+    args = (dev(a), dev(sa), dev(w), dev(sw), dev_bf16(bias))
+    ig = Guarded((M, N), torch.int32)
+    bg = Guarded((M, N), torch.bfloat16)
+    B.gemm(*args, out_dtype=torch.int32, out=ig.t)
+    B.gemm(*args, out_dtype=torch.bfloat16, out=bg.t)
+    torch.cuda.synchronize()
+    got = ig.t.cpu().numpy()
+    yb = host_bf16(bg.t)
+    ig.check()
+    bg.check()
+    want = orc.gemm_i32(a, w)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} accumulators differ: {bad[:5].tolist()}"
+    _, rb = orc.epilogue(want, sa, sw, bias)
+    assert np.array_equal(yb, rb)
+
+
 @pytest.mark.parametrize("M,N", [(3, 256), (300, 512), (1100, 2048),
                                  (4097, 4096)])
 def test_gemm_max_k_closed_form(M, N):
