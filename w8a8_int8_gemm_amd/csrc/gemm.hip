@@ -646,15 +646,15 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(
 // Large M: 256x256 tiles, 8 waves (two per SIMD) of 64x128, two slots of
 // 128-byte K stages (128 KiB LDS): each direct load then fills whole
 // 128-byte lines of 8 rows, where 64-byte stages used half lines of 16 rows
-// (5% faster on the DiT shapes).  Small M: 64x128 tiles, 4 waves of 64x32:
-// a 4-slot ring of 64-byte stages when few tiles split K (more stages in
-// flight per byte), two slots of 128-byte stages when the tiles fill the
-// chip unsplit.
+// (5% faster on the DiT shapes).  Small M: 64x128 tiles, 4 waves of 64x32,
+// 128-byte stages: a 4-slot ring (96 KiB, three stages in flight) when few
+// tiles split K, two slots (48 KiB, three work groups per CU) when the
+// tiles fill the chip unsplit.
 #ifndef W8A8_CFG_LARGE
 #define W8A8_CFG_LARGE 256, 256, 128, 4, 2, 4, 2
 #endif
 #ifndef W8A8_CFG_SKINNY
-#define W8A8_CFG_SKINNY 64, 128, 64, 1, 4, 1, 4
+#define W8A8_CFG_SKINNY 64, 128, 128, 1, 4, 1, 4
 #endif
 #ifndef W8A8_CFG_MID
 #define W8A8_CFG_MID 64, 128, 128, 1, 4, 1, 2
@@ -800,7 +800,7 @@ constexpr int kCUs = 256;
 #define W8A8_SKINNY_WGS_PER_CU 1
 #endif
 #ifndef W8A8_SKINNY_MIN_STAGES
-#define W8A8_SKINNY_MIN_STAGES 8
+#define W8A8_SKINNY_MIN_STAGES 4
 #endif
 // Fewest K slices that make a split tail launch worthwhile, and the least
 // K (bytes) of one slice.
