@@ -34,7 +34,9 @@
 #include "internal.h"
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
+#include <unordered_map>
 
 #pragma clang fp contract(off)
 
@@ -672,11 +674,27 @@ void launch_main(const KernelArgs &p, dim3 grid, hipStream_t stream) {
                      stream, p);
 }
 
+// Dynamic LDS above 64 KiB needs an explicit opt-in: once per device for
+// each configuration (the result is kept, errors included).
+template <class C>
+hipError_t ensure_lds_limit() {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::unordered_map<int, hipError_t> done;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = done.find(dev);
+  if (it != done.end()) return it->second;
+  const hipError_t r = set_lds_limit<C>();
+  done[dev] = r;
+  return r;
+}
+
 template <class C>
 hipError_t launch_cfg(const GemmArgs &g, const GemmPlan &plan,
                       hipStream_t stream) {
-  // Dynamic LDS above 64 KiB needs an explicit opt-in, once per process.
-  static const hipError_t lds_ok = set_lds_limit<C>();
+  const hipError_t lds_ok = ensure_lds_limit<C>();
   if (lds_ok != hipSuccess) return lds_ok;
   KernelArgs p;
   p.a = g.a;
