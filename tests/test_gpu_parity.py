@@ -584,6 +584,39 @@ def test_block_sampled_rows(orc, config):
     assert np.array_equal(host_bf16(out["fc2"][ri]), ref["fc2"])
 
 
+# configs 4 and 6 chain 50 blocks through the power-of-two renormalization;
+# the first two blocks of each chain (distinct weights per block) are
+# checked on sampled rows, including the renormalized block input.
+@pytest.mark.parametrize("config", [4, 6])
+def test_chain_sampled_rows(orc, config):
+    wl = D.WORKLOADS[config]
+    say(f"chain config {config}: {wl.name} M={wl.M}, first 2 blocks")
+    x = D.activations(wl.M, D.HIDDEN, wl.seed)
+    rows = D.row_sample(wl.M, 14, wl.seed)
+    ri = torch.from_numpy(rows).cuda()
+    runner = BL.BlockRunner(wl.M, projs=wl.projs, mlp=wl.mlp,
+                            o_input=wl.o_input)
+    xd = dev_bf16(x)
+    bufs = [torch.empty_like(xd), torch.empty_like(xd)]
+    xr = x[rows]
+    for b in range(2):
+        params = D.block_params(wl, b)
+        projs = {p.name: BL.upload_proj(p, params[p.name]) for p in wl.projs}
+        out = runner.run(xd, projs)
+        ref = oracle_block_rows(orc, xr, params, wl.mlp, wl.o_input)
+        torch.cuda.synchronize()
+        for n in ("q", "o", "fc1", "fc2"):
+            assert np.array_equal(host_bf16(out[n][ri]), ref[n]), (b, n)
+        if b == 0:
+            nxt = bufs[0]
+            B.pow2_renorm(out["fc2"], out=nxt)
+            torch.cuda.synchronize()
+            xr = orc.pow2_renorm(ref["fc2"])
+            assert np.array_equal(host_bf16(nxt[ri]), xr)
+            xd = nxt
+        del projs, params
+
+
 def test_gemm_epilogue_edge_values(orc):
     """Accumulators, scales and biases chosen to hit BF16 ties, results
     that are FP32/BF16 subnormal, the bias-before-rounding case and
