@@ -534,19 +534,19 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
   for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < quads;
        q += (int64_t)gridDim.x * 256) {
     const int64_t o = q * 4;
-    // Four slices' loads in flight at a time (a serial chain of loads
-    // would wait out one memory latency per slice).
-    v4i s = *reinterpret_cast<const v4i *>(part + o);
-    int z = 1;
-    for (; z + 4 <= splits; z += 4) {
-      const v4i a = *reinterpret_cast<const v4i *>(part + z * MN + o);
-      const v4i b = *reinterpret_cast<const v4i *>(part + (z + 1) * MN + o);
-      const v4i c = *reinterpret_cast<const v4i *>(part + (z + 2) * MN + o);
-      const v4i d = *reinterpret_cast<const v4i *>(part + (z + 3) * MN + o);
-      s += (a + b) + (c + d);
+    // Up to eight slices' loads in flight at a time (a serial chain of
+    // loads would wait out one memory latency per slice).
+    v4i s = v4i{0, 0, 0, 0};
+    for (int z0 = 0; z0 < splits; z0 += 8) {
+      v4i v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        v[i] = z0 + i < splits
+                   ? *reinterpret_cast<const v4i *>(part + (z0 + i) * MN + o)
+                   : v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += v[i];
     }
-    for (; z < splits; ++z)
-      s += *reinterpret_cast<const v4i *>(part + z * MN + o);
     if (EPI == EPI_I32) {
       *reinterpret_cast<v4i *>(static_cast<int *>(out) + o) = s;
       continue;
@@ -603,16 +603,17 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(
   const int64_t tile_elems = (int64_t)C::BM * C::BN;
   const int *src = part + (int64_t)t * tile_elems + q * 4;
   const int64_t zs = (int64_t)ntail * tile_elems;  // between slices
-  v4i s = *reinterpret_cast<const v4i *>(src);
-  int z = 1;
-  for (; z + 4 <= splits; z += 4) {
-    const v4i a = *reinterpret_cast<const v4i *>(src + z * zs);
-    const v4i b = *reinterpret_cast<const v4i *>(src + (z + 1) * zs);
-    const v4i c = *reinterpret_cast<const v4i *>(src + (z + 2) * zs);
-    const v4i d = *reinterpret_cast<const v4i *>(src + (z + 3) * zs);
-    s += (a + b) + (c + d);
+  v4i s = v4i{0, 0, 0, 0};
+  for (int z0 = 0; z0 < splits; z0 += 8) {  // eight slices' loads in flight
+    v4i v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      v[i] = z0 + i < splits
+                 ? *reinterpret_cast<const v4i *>(src + (z0 + i) * zs)
+                 : v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += v[i];
   }
-  for (; z < splits; ++z) s += *reinterpret_cast<const v4i *>(src + z * zs);
   const int64_t o = (int64_t)m * N + n;
   if (EPI == EPI_I32) {
     *reinterpret_cast<v4i *>(static_cast<int *>(out) + o) = s;
