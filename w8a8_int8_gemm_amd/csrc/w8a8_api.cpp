@@ -53,16 +53,16 @@ int check_device() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return W8A8_ERR_DEVICE;
   static std::mutex mu;
-  static std::unordered_map<int, int> verdict;
+  static std::unordered_map<int, int> checked;
   std::lock_guard<std::mutex> lock(mu);
-  auto it = verdict.find(dev);
-  if (it != verdict.end()) return it->second;
+  auto it = checked.find(dev);
+  if (it != checked.end()) return it->second;
   hipDeviceProp_t prop;
   int status = W8A8_ERR_DEVICE;
   if (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
       std::strncmp(prop.gcnArchName, "gfx950", 6) == 0)
     status = W8A8_OK;
-  verdict[dev] = status;
+  checked[dev] = status;
   return status;
 }
 
