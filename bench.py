@@ -19,7 +19,10 @@ Inputs and weights are resident in HBM before timing starts.  Reported:
                5.0 POP/s;
   cpu_baseline = the CPU oracle timed on a bounded row sample;
   bf16_baseline (context) = torch's BF16 linear (hipBLASLt) on the same
-               shapes.
+               shapes;
+  int8_library_baseline (context) = hipBLASLt's INT8 GEMM (torch._int_mm)
+               on the same codes and weights: INT32 accumulators only, no
+               scales, bias or BF16 rounding.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 0-6]
        [--fused-qkv]
 """
@@ -57,6 +60,7 @@ def parse():
     ap.add_argument("--config", type=int, default=4, choices=range(7))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
+    ap.add_argument("--no-int8-library-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--check-rows", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -312,6 +316,19 @@ def main():
                              args.warmup, max(args.steps, 3))
         log(f"[bench] BF16 baseline: {bf16['tflops']:.1f} TFLOPS")
 
+    # ---- INT8 library baseline (hipBLASLt through torch), same codes
+    int8lib = None
+    if not args.no_int8_library_baseline:
+        if single:
+            codes = {wl.projs[0].name: qbuf}
+        else:
+            codes = runner.codes_by_projection(blocks[0])
+        int8lib = int8_library_baseline(torch, blocks[0], codes, M,
+                                        args.warmup, max(args.steps, 3),
+                                        gemm_tops)
+        log(f"[bench] INT8 library baseline: {int8lib['tops']:.1f} TOPS "
+            f"(w8a8_gemm {int8lib['w8a8_gemm_speedup']:.3f}x)")
+
     # ---- CPU baseline: the oracle on a bounded row sample
     cpu = None
     if not args.no_cpu_baseline:
@@ -348,6 +365,7 @@ def main():
                                    traffic_entry(wl, args.fused_qkv)),
         "cpu_baseline": cpu,
         "bf16_baseline": bf16,
+        "int8_library_baseline": int8lib,
         "oracle_check": check,
     }
     print(json.dumps(result), flush=True)
@@ -467,6 +485,39 @@ def bf16_baseline(torch, D, BL, wl, x0, blk, dev, warmup, reps):
             "pct_bf16_peak": round(100 * tflops / BF16_PEAK_TFLOPS, 2),
             "what": "torch.nn.functional.linear, BF16 weights, one block "
                     "(SiLU or SwiGLU included)"}
+
+
+def int8_library_baseline(torch, blk, codes, M, warmup, reps, gemm_tops):
+    """hipBLASLt's INT8 GEMM through torch._int_mm on one block's shapes,
+    fed the codes the step's own quantizations produced and the resident
+    INT8 weights (consumed transposed, as stored).  It returns INT32
+    accumulators only: no per-token / per-channel scales, no bias and no
+    BF16 rounding, and it writes 4 bytes per output against w8a8_gemm's 2."""
+    calls = [(codes[n], p.w) for n, p in blk.items()]
+    ops = sum(2 * M * p.N * p.K for p in blk.values())
+
+    def run():
+        for q, w in calls:
+            torch._int_mm(q, w.t())
+
+    for _ in range(warmup + 1):
+        run()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        run()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    tops = ops / (ms * 1e-3) / 1e12
+    return {"tops": round(tops, 2), "ms_per_block": round(ms, 4),
+            "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
+            "w8a8_gemm_speedup": round(gemm_tops / tops, 3)
+            if gemm_tops else None,
+            "what": "torch._int_mm (hipBLASLt), INT32 output only, same "
+                    "codes and weights, one block's GEMMs"}
 
 
 def oracle_block_rows(orc, wl, params, x_rows):

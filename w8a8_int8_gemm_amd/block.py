@@ -131,6 +131,15 @@ class BlockRunner:
         self._gemm(projs, "fc2", self.hq, self.hs, stream, on_gemm)
         return self.out
 
+    def codes_by_projection(self, projs: dict) -> dict:
+        """The INT8 input codes each projection of ``projs`` read in the
+        last ``run`` (the buffers, not copies)."""
+        src = {"q": self.xq[0], "k": self.xq[0], "v": self.xq[0],
+               "qkv": self.xq[0],
+               "o": self.oq if self.o_input == "v" else self.xq[1],
+               "fc1": self.xq[2], "fc2": self.hq}
+        return {n: src[n] for n in projs}
+
     def run(self, x, projs: dict, stream=None, on_gemm=None):
         """x: bf16 [M, H].  Returns the dict of BF16 outputs."""
         def gemm(name, q, s):
