@@ -22,7 +22,12 @@ Inputs and weights are resident in HBM before timing starts.  Reported:
                shapes;
   int8_library_baseline (context) = hipBLASLt's INT8 GEMM (torch._int_mm)
                on the same codes and weights: INT32 accumulators only, no
-               scales, bias or BF16 rounding.
+               scales, bias or BF16 rounding;
+  mfma_ceiling (context, MFMA-bound workloads) = the rate of the GEMM's
+               MFMA sequence with register operands only (no memory
+               traffic), on the workload's own codes and weights: the
+               board's power limit makes the matrix cores' sustained rate
+               depend on the data.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 0-6]
        [--fused-qkv]
 """
@@ -61,6 +66,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
     ap.add_argument("--no-int8-library-baseline", action="store_true")
+    ap.add_argument("--no-mfma-ceiling", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--check-rows", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -329,6 +335,22 @@ def main():
         log(f"[bench] INT8 library baseline: {int8lib['tops']:.1f} TOPS "
             f"(w8a8_gemm {int8lib['w8a8_gemm_speedup']:.3f}x)")
 
+    # ---- register-only MFMA rate on the same codes and weights
+    ceiling = None
+    roofline = roofline_entry(blocks[0], M, gemm_tops, avg_launch_us,
+                              launches, use_graph,
+                              traffic_entry(wl, args.fused_qkv))
+    if not args.no_mfma_ceiling and roofline["bound"] == "mfma":
+        if single:
+            xc, wc = qbuf, blocks[0][wl.projs[0].name].w
+        else:
+            xc, wc = runner.xq[0], blocks[0]["qkv" if args.fused_qkv
+                                          else "q"].w
+        ceiling = mfma_ceiling(torch, xc, wc, gemm_tops)
+        log(f"[bench] MFMA ceiling on the workload's codes: "
+            f"{ceiling['tops']:.1f} TOPS; the GEMM reaches "
+            f"{ceiling['gemm_frac_of_ceiling']:.3f} of it")
+
     # ---- CPU baseline: the oracle on a bounded row sample
     cpu = None
     if not args.no_cpu_baseline:
@@ -360,12 +382,11 @@ def main():
             "parallelism": "single_gpu",
         },
         "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
-        "roofline": roofline_entry(blocks[0], M, gemm_tops, avg_launch_us,
-                                   launches, use_graph,
-                                   traffic_entry(wl, args.fused_qkv)),
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "bf16_baseline": bf16,
         "int8_library_baseline": int8lib,
+        "mfma_ceiling": ceiling,
         "oracle_check": check,
     }
     print(json.dumps(result), flush=True)
@@ -518,6 +539,61 @@ def int8_library_baseline(torch, blk, codes, M, warmup, reps, gemm_tops):
             if gemm_tops else None,
             "what": "torch._int_mm (hipBLASLt), INT32 output only, same "
                     "codes and weights, one block's GEMMs"}
+
+
+def mfma_ceiling(torch, x_codes, w_codes, gemm_tops, blocks=1024,
+                 iters=2048, reps=20):
+    """Sustained rate of the GEMM's v_mfma_i32_32x32x32_i8 sequence with
+    register operands only, fed fragments of the given token codes and
+    weights (libw8a8_ceiling.so, a measurement kernel outside the library):
+    8 waves per CU, 1024 work groups per launch, `reps` launches back to
+    back after a warm one, so the board reaches its power-limited clock."""
+    import ctypes
+    from w8a8_int8_gemm_amd import build as LB
+    if not LB.CEILING_LIB.exists():
+        raise RuntimeError(f"{LB.CEILING_LIB} is not built "
+                           "(run __graft_entry__.build())")
+    lib = ctypes.CDLL(str(LB.CEILING_LIB))
+    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.w8a8_ceiling_run.restype = ci
+    lib.w8a8_ceiling_run.argtypes = [vp, i64, vp, i64, i64, ci, ci, vp, vp]
+    lib.w8a8_ceiling_ops.restype = ctypes.c_double
+    lib.w8a8_ceiling_ops.argtypes = [ci, ci]
+    lib.w8a8_ceiling_out_len.restype = i64
+    lib.w8a8_ceiling_out_len.argtypes = [ci]
+    if x_codes.shape[1] != w_codes.shape[1]:
+        raise ValueError("codes and weights disagree on K")
+    out = torch.empty((lib.w8a8_ceiling_out_len(blocks),), dtype=torch.int32,
+                      device=x_codes.device)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run():
+        rc = lib.w8a8_ceiling_run(
+            x_codes.data_ptr(), x_codes.shape[0], w_codes.data_ptr(),
+            w_codes.shape[0], x_codes.shape[1], blocks, iters,
+            out.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(f"w8a8_ceiling_run failed ({rc})")
+
+    run()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        run()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    tops = lib.w8a8_ceiling_ops(blocks, iters) / (ms * 1e-3) / 1e12
+    return {"tops": round(tops, 2),
+            "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
+            "gemm_frac_of_ceiling": round(gemm_tops / tops, 4)
+            if gemm_tops else None,
+            "what": "v_mfma_i32_32x32x32_i8, the GEMM's MFMA order, register "
+                    "operands only (4 k-steps of 2 token and 4 weight "
+                    "fragments per wave, 8 waves per CU), on the workload's "
+                    "token codes and weights"}
 
 
 def oracle_block_rows(orc, wl, params, x_rows):

@@ -228,3 +228,33 @@ def test_binding_checks_tensors_before_calling():
         B.quantize_act(torch.zeros((4, 128), dtype=torch.float32))
     with pytest.raises(TypeError):
         B.pow2_renorm([[1.0]])
+
+
+def test_mfma_ceiling_library_host_side():
+    """The measurement kernel's library (outside the W8A8 ABI) loads,
+    counts its operations in closed form and rejects arguments its kernel
+    cannot take without launching anything."""
+    from w8a8_int8_gemm_amd import build as LB
+    lib = ctypes.CDLL(str(LB.CEILING_LIB))
+    lib.w8a8_ceiling_ops.restype = ctypes.c_double
+    lib.w8a8_ceiling_ops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.w8a8_ceiling_out_len.restype = ctypes.c_int64
+    lib.w8a8_ceiling_out_len.argtypes = [ctypes.c_int]
+    lib.w8a8_ceiling_run.restype = ctypes.c_int
+    lib.w8a8_ceiling_run.argtypes = [ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_int64, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    # 8 waves x 32 MFMAs of 2*32*32*32 operations per round
+    assert lib.w8a8_ceiling_ops(3, 5) == 3 * 8 * 5 * 32 * 65536
+    assert lib.w8a8_ceiling_out_len(7) == 7 * 512
+    ok = dict(x=BUF["aq"], xr=64, w=BUF["w"], wr=64, K=256, blocks=1,
+              iters=1, out=BUF["out"])
+    for bad in [dict(x=None), dict(w=None), dict(out=None), dict(xr=31),
+                dict(wr=0), dict(K=127), dict(K=136), dict(blocks=0),
+                dict(iters=0)]:
+        a = {**ok, **bad}
+        assert lib.w8a8_ceiling_run(a["x"], a["xr"], a["w"], a["wr"], a["K"],
+                                    a["blocks"], a["iters"], a["out"],
+                                    None) == 1, bad

@@ -23,6 +23,10 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libw8a8.so"
 SOURCES = ["w8a8_api.cpp", "rowwise.hip", "gemm.hip"]
+# Measurement support, not part of the library: the register-only MFMA
+# rate on given code matrices (loaded by bench.py only).
+CEILING_LIB = PKG / "libw8a8_ceiling.so"
+CEILING_SOURCES = ["mfma_ceiling.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -35,11 +39,11 @@ FLAGS = [
 
 
 def build(extra: list[str] | None = None, out: Path = LIB,
-          verbose: bool = False) -> Path:
+          verbose: bool = False, sources: list[str] | None = None) -> Path:
     """Compile every HIP source of the library into one shared object."""
     tmp = out.with_name(out.name + ".tmp")
     cmd = [HIPCC, *FLAGS, *(extra or []), "-o", str(tmp),
-           *[str(CSRC / s) for s in SOURCES]]
+           *[str(CSRC / s) for s in (sources or SOURCES)]]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,5 +57,11 @@ def build(extra: list[str] | None = None, out: Path = LIB,
     return out
 
 
+def build_ceiling(verbose: bool = False) -> Path:
+    """Compile the MFMA-ceiling measurement kernel (libw8a8_ceiling.so)."""
+    return build(out=CEILING_LIB, verbose=verbose, sources=CEILING_SOURCES)
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_ceiling(verbose=True))
