@@ -3,7 +3,8 @@
 
 A step is one pass of the whole hot path over the workload's synthetic
 input, all of it in the library's HIP kernels on one stream:
-  per block: quantize X (shared by Q, K, V) -> 3 GEMMs; quantize X -> O GEMM;
+  per block: quantize X (shared by Q, K, V) -> Q, K and V (one GEMM over
+  the concatenated weights where O reads X, else three); quantize X -> O GEMM;
   quantize X -> FC1 GEMM; SiLU+quantize of FC1's output -> FC2 GEMM;
   between blocks (the sweep): power-of-two renormalization of FC2's output
   feeds the next block.
@@ -29,7 +30,7 @@ Inputs and weights are resident in HBM before timing starts.  Reported:
                board's power limit makes the matrix cores' sustained rate
                depend on the data.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 0-6]
-       [--fused-qkv]
+       [--qkv auto|fused|separate]
 """
 from __future__ import annotations
 
@@ -70,9 +71,15 @@ def parse():
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--check-rows", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--fused-qkv", action="store_true",
-                    help="run Q, K and V as one GEMM over the concatenated "
-                         "weights [3N, K] (same outputs, bit for bit)")
+    ap.add_argument("--qkv", choices=("auto", "fused", "separate"),
+                    default="auto",
+                    help="fused: Q, K and V as one GEMM over the "
+                         "concatenated weights [3N, K] (the same outputs, "
+                         "bit for bit); separate: three GEMMs; auto (the "
+                         "default): fused wherever the attention output "
+                         "projection reads the block input X")
+    ap.add_argument("--fused-qkv", dest="qkv", action="store_const",
+                    const="fused", help="the same as --qkv fused")
     ap.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
                     help="replay the step (and the GEMM-only timing) as a "
                          "HIP graph; auto = on for the single-projection "
@@ -125,6 +132,11 @@ def main():
     wl = D.WORKLOADS[args.config]
     M = wl.M
     single = len(wl.projs) == 1
+    if args.qkv == "fused" and (single or wl.o_input != "x"):
+        raise SystemExit("--qkv fused needs a block workload whose attention "
+                         "output projection reads X")
+    fused = (not single and wl.o_input == "x" and
+             args.qkv in ("auto", "fused"))
     threads = min(16, os.cpu_count() or 8)
 
     # ---- oracle sample (row chain), computed while weights are on the host
@@ -146,10 +158,7 @@ def main():
         params = D.block_params(wl, b, threads=threads)
         dblk = {p.name: BL.upload_proj(p, params[p.name], dev)
                 for p in wl.projs}
-        if args.fused_qkv and not single:
-            if wl.o_input != "x":
-                raise SystemExit("--fused-qkv needs a workload whose "
-                                 "attention output projection reads X")
+        if fused:
             dblk = BL.fuse_qkv(dblk)
         blocks.append(dblk)
         if rows is not None:
@@ -169,7 +178,7 @@ def main():
 
     x0 = BL.to_device_bf16(x0_host, dev)
     xbuf = [torch.empty_like(x0), torch.empty_like(x0)]
-    runner = (BL.BlockRunner(M, dev, fused_qkv=args.fused_qkv,
+    runner = (BL.BlockRunner(M, dev, fused_qkv=fused,
                              projs=wl.projs, mlp=wl.mlp, o_input=wl.o_input)
               if not single else None)
     if single:
@@ -339,13 +348,12 @@ def main():
     ceiling = None
     roofline = roofline_entry(blocks[0], M, gemm_tops, avg_launch_us,
                               launches, use_graph,
-                              traffic_entry(wl, args.fused_qkv))
+                              traffic_entry(wl, fused))
     if not args.no_mfma_ceiling and roofline["bound"] == "mfma":
         if single:
             xc, wc = qbuf, blocks[0][wl.projs[0].name].w
         else:
-            xc, wc = runner.xq[0], blocks[0]["qkv" if args.fused_qkv
-                                          else "q"].w
+            xc, wc = runner.xq[0], blocks[0]["qkv" if fused else "q"].w
         ceiling = mfma_ceiling(torch, xc, wc, gemm_tops)
         log(f"[bench] MFMA ceiling on the workload's codes: "
             f"{ceiling['tops']:.1f} TOPS; the GEMM reaches "
@@ -373,8 +381,7 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {
-            "workload": wl.name + ("+fused_qkv" if args.fused_qkv and
-                                   not single else ""),
+            "workload": wl.name + ("+fused_qkv" if fused else ""),
             "tokens": M,
             "blocks": wl.blocks,
             "linears": wl.blocks * len(wl.projs),
@@ -433,23 +440,34 @@ def roofline_entry(blk, M, gemm_tops, avg_launch_us, launches, graph,
     }
 
 
+def gemm_mix(wl, fused_qkv):
+    """(tokens, sorted (N, K) of a block's GEMM calls) for a workload, with
+    Q, K and V as one [3N, K] call when fused."""
+    shapes = [(p.N, p.K) for p in wl.projs
+              if not (fused_qkv and p.name in ("q", "k", "v"))]
+    if fused_qkv:
+        q = next(p for p in wl.projs if p.name == "q")
+        shapes.append((3 * q.N, q.K))
+    return wl.M, sorted(shapes)
+
+
 def traffic_entry(wl, fused_qkv):
     """Measured HBM bytes per GEMM launch from committed rocprofv3 counter
-    summaries: valid only for the projection mix they were taken on (the
-    six calls of a block at its token count and shapes) and only while the
+    summaries: each record is valid only for the call mix it was taken on
+    (a block's GEMM calls at its token count and shapes) and only while the
     kernel source is unchanged."""
     f = ROOT / "profiles" / "gemm_traffic.json"
-    if not f.exists() or fused_qkv:
+    if not f.exists():
         return None
-    rec = json.loads(f.read_text())
-    if rec.get("kernel_sha256") != kernel_source_sha256():
-        return None
-    mix = rec.get("workload", {})
-    if (mix.get("tokens") != wl.M or
-            sorted(map(tuple, mix.get("shapes_NK", []))) !=
-            sorted((p.N, p.K) for p in wl.projs)):
-        return None
-    return rec.get("traffic")
+    tokens, shapes = gemm_mix(wl, fused_qkv)
+    for rec in json.loads(f.read_text()).get("records", []):
+        if rec.get("kernel_sha256") != kernel_source_sha256():
+            continue
+        mix = rec.get("workload", {})
+        if (mix.get("tokens") == tokens and
+                sorted(map(tuple, mix.get("shapes_NK", []))) == shapes):
+            return rec.get("traffic")
+    return None
 
 
 def kernel_source_sha256():

@@ -57,13 +57,25 @@ def test_roofline_hbm_bound_single_projection():
 
 
 def test_traffic_only_for_its_projection_mix():
-    rec = json.loads((ROOT / "profiles" / "gemm_traffic.json").read_text())
+    recs = json.loads(
+        (ROOT / "profiles" / "gemm_traffic.json").read_text())["records"]
+    sha = bench.kernel_source_sha256()
     wl2 = D.WORKLOADS[2]
-    t = bench.traffic_entry(wl2, False)
-    if rec["kernel_sha256"] == bench.kernel_source_sha256():
-        assert t == rec["traffic"]
-    else:  # taken on an older kernel: not reported
-        assert t is None
-    assert bench.traffic_entry(wl2, True) is None          # fused QKV mix
+    for fused in (False, True):
+        tokens, shapes = bench.gemm_mix(wl2, fused)
+        match = [r for r in recs if r["kernel_sha256"] == sha and
+                 r["workload"]["tokens"] == tokens and
+                 sorted(map(tuple, r["workload"]["shapes_NK"])) == shapes]
+        t = bench.traffic_entry(wl2, fused)
+        # a record taken on an older kernel, or none for this mix: no traffic
+        assert t == (match[0]["traffic"] if match else None)
     assert bench.traffic_entry(D.WORKLOADS[0], False) is None  # M = 64
     assert bench.traffic_entry(D.WORKLOADS[5], False) is None  # page shapes
+
+
+def test_gemm_mix_fuses_qkv_into_one_call():
+    tokens, sep = bench.gemm_mix(D.WORKLOADS[2], False)
+    _, fused = bench.gemm_mix(D.WORKLOADS[2], True)
+    assert tokens == 19077 and len(sep) == 6 and len(fused) == 4
+    assert (3 * 5376, 5376) in fused and sep.count((5376, 5376)) == 4
+    assert sum(n for n, _ in sep) == sum(n for n, _ in fused)
