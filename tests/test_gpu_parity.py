@@ -558,15 +558,21 @@ def test_config0_single_projection(orc):
 # configs 1-3: the block at 4096, 19077 and 37503 tokens; 5: the pages' H3
 # operator shapes (Q/K/V 5376 -> 7168, O fed by V, SwiGLU over a fused
 # gate | up FC1 5376 -> 28672, FC2 14336 -> 5376) at 19077 tokens.
-@pytest.mark.parametrize("config", [1, 2, 3, 5])
-def test_block_sampled_rows(orc, config):
+# Where O reads X (configs 1-3) Q, K and V also run fused into one GEMM,
+# as the benchmark runs them.
+@pytest.mark.parametrize("config,fused", [(1, False), (2, False), (3, False),
+                                          (5, False), (1, True), (2, True),
+                                          (3, True)])
+def test_block_sampled_rows(orc, config, fused):
     wl = D.WORKLOADS[config]
-    say(f"block config {config}: {wl.name} M={wl.M}")
+    say(f"block config {config}: {wl.name} M={wl.M}, fused QKV {fused}")
     params = D.block_params(wl, 0)
     projs = {p.name: BL.upload_proj(p, params[p.name]) for p in wl.projs}
+    if fused:
+        projs = BL.fuse_qkv(projs)
     x = D.activations(wl.M, D.HIDDEN, wl.seed)
-    runner = BL.BlockRunner(wl.M, projs=wl.projs, mlp=wl.mlp,
-                            o_input=wl.o_input)
+    runner = BL.BlockRunner(wl.M, fused_qkv=fused, projs=wl.projs,
+                            mlp=wl.mlp, o_input=wl.o_input)
     out = runner.run(dev_bf16(x), projs)
     torch.cuda.synchronize()
     rows = D.row_sample(wl.M, 24, wl.seed)
@@ -587,21 +593,24 @@ def test_block_sampled_rows(orc, config):
 # configs 4 and 6 chain 50 blocks through the power-of-two renormalization;
 # the first two blocks of each chain (distinct weights per block) are
 # checked on sampled rows, including the renormalized block input.
-@pytest.mark.parametrize("config", [4, 6])
-def test_chain_sampled_rows(orc, config):
+@pytest.mark.parametrize("config,fused", [(4, True), (6, False)])
+def test_chain_sampled_rows(orc, config, fused):
     wl = D.WORKLOADS[config]
-    say(f"chain config {config}: {wl.name} M={wl.M}, first 2 blocks")
+    say(f"chain config {config}: {wl.name} M={wl.M}, first 2 blocks, "
+        f"fused QKV {fused}")
     x = D.activations(wl.M, D.HIDDEN, wl.seed)
     rows = D.row_sample(wl.M, 14, wl.seed)
     ri = torch.from_numpy(rows).cuda()
-    runner = BL.BlockRunner(wl.M, projs=wl.projs, mlp=wl.mlp,
-                            o_input=wl.o_input)
+    runner = BL.BlockRunner(wl.M, fused_qkv=fused, projs=wl.projs,
+                            mlp=wl.mlp, o_input=wl.o_input)
     xd = dev_bf16(x)
     bufs = [torch.empty_like(xd), torch.empty_like(xd)]
     xr = x[rows]
     for b in range(2):
         params = D.block_params(wl, b)
         projs = {p.name: BL.upload_proj(p, params[p.name]) for p in wl.projs}
+        if fused:
+            projs = BL.fuse_qkv(projs)
         out = runner.run(xd, projs)
         ref = oracle_block_rows(orc, xr, params, wl.mlp, wl.o_input)
         torch.cuda.synchronize()
