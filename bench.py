@@ -7,7 +7,7 @@ input, all of it in the library's HIP kernels on one stream:
   the concatenated weights where O reads X, else three); quantize X -> O GEMM;
   quantize X -> FC1 GEMM; SiLU+quantize of FC1's output -> FC2 GEMM;
   between blocks (the sweep): power-of-two renormalization of FC2's output
-  feeds the next block.
+  feeds the next block, fused with that block's quantization for Q, K, V.
 Inputs and weights are resident in HBM before timing starts.  Reported:
   value      = sum of 2*M*N*K over the step's GEMMs / step time (TOPS),
                quantization and glue time included, from K steps timed
@@ -216,10 +216,12 @@ def main():
         x = x0
         out = None
         for b, blk in enumerate(blocks):
-            out = runner.run(x, blk, on_gemm=on_gemm)
+            out = runner.run(x, blk, on_gemm=on_gemm, x_quantized=b > 0)
             if b + 1 < len(blocks):
+                # the next block's input and its quantization for Q, K, V
                 nxt = xbuf[b % 2]
-                B.pow2_renorm(out["fc2"], out=nxt)
+                B.pow2_renorm_quantize(out["fc2"], out=(nxt, runner.xq[0],
+                                                        runner.xs[0]))
                 x = nxt
         return out
 

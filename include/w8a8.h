@@ -193,6 +193,14 @@ int w8a8_last_hip_error(void);
  *   while keeping BF16 activations finite.  K % 8 == 0, 16-byte aligned;
  *   in place allowed.
  *
+ * w8a8_pow2_renorm_quantize: w8a8_pow2_renorm of x into y followed by
+ *   w8a8_quantize_act of y, in one pass over x: y BF16 [M,K] is written
+ *   and a_q INT8 [M,K], a_scale FP32 [M] are exactly what
+ *   w8a8_quantize_act(y) produces.  x, y 16-byte aligned, a_q 8-byte,
+ *   a_scale 4-byte; 8 <= K <= 90112, K % 8 == 0; y may be x (in place) but
+ *   must not partially overlap it; a_q and a_scale overlap nothing.
+ *   Errors as w8a8_quantize_act.
+ *
  * w8a8_quantize_act_silu: w8a8_silu_bf16 followed by w8a8_quantize_act in
  *   one pass over x (the SiLU values are rounded to BF16 before they are
  *   quantized, exactly as the two separate calls do); the BF16 SiLU output
@@ -224,6 +232,9 @@ int w8a8_quantize_act_swiglu(const uint16_t *h, int64_t M, int64_t F,
                              int8_t *a_q, float *a_scale, void *stream);
 int w8a8_pow2_renorm(const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                      void *stream);
+int w8a8_pow2_renorm_quantize(const uint16_t *x, int64_t M, int64_t K,
+                              uint16_t *y, int8_t *a_q, float *a_scale,
+                              void *stream);
 int w8a8_quantize_act_silu(const uint16_t *x, int64_t M, int64_t K,
                            int8_t *a_q, float *a_scale, void *stream);
 

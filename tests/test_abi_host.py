@@ -196,6 +196,26 @@ def test_weight_and_gated_glue_reject():
     assert qs(BUF["x"], 2, 64, BUF["x"] + 128, BUF["sa"], None) == ALIAS
 
 
+def test_renorm_quantize_rejects():
+    lib = B.lib()
+    rq = lib.w8a8_pow2_renorm_quantize
+    x, y, q, sa = BUF["x"], BUF["out"], BUF["aq"], BUF["sa"]
+    assert rq(None, 4, 64, y, q, sa, None) == NULL
+    assert rq(x, 4, 64, y, None, sa, None) == NULL
+    assert rq(x, 4, 64, y, q, None, None) == NULL
+    assert rq(x, 0, 64, y, q, sa, None) == SHAPE
+    assert rq(x, 4, 60, y, q, sa, None) == SHAPE
+    assert rq(x, 4, B.QUANT_MAX_K + 8, y, q, sa, None) == SHAPE
+    assert rq(x + 8, 4, 64, y, q, sa, None) == ALIGN
+    assert rq(x, 4, 64, y + 8, q, sa, None) == ALIGN
+    assert rq(x, 4, 64, y, q + 4, sa, None) == ALIGN
+    assert rq(x, 4, 64, y, q, sa + 2, None) == ALIGN
+    assert rq(x, 4, 64, x + 16, q, sa, None) == ALIAS   # y partly over x
+    assert rq(x, 4, 64, y, x + 64, sa, None) == ALIAS   # codes over x
+    assert rq(x, 4, 64, y, y + 256, sa, None) == ALIAS  # codes over y
+    assert rq(x, 4, 64, y, q, q + 64, None) == ALIAS    # scales over codes
+
+
 def test_no_device_is_reported_without_a_gpu():
     """Valid arguments on a machine without a GPU: the device check, the
     last step before any launch, refuses.  Skipped where a GPU exists

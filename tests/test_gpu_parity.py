@@ -165,6 +165,38 @@ def test_pow2_renorm(orc, M, K):
     assert np.array_equal(y, orc.pow2_renorm(x))
 
 
+@pytest.mark.parametrize("M,K,in_place", [(6, 5376, False), (9, 21504, False),
+                                          (5, 8, False), (4200, 5376, False),
+                                          (7, 5376, True), (3, 21504, True)])
+def test_pow2_renorm_quantize(orc, M, K, in_place):
+    """One pass = the renormalization, then the quantization of its BF16
+    output, exactly as the oracle's two steps."""
+    say(f"pow2_renorm_quantize M={M} K={K} in place {in_place}")
+    x = D.activations(M, K, seed=8)
+    x[0] = 0
+    x[1, :3] = [0x0001, 0x8003, 0x0002]      # subnormal-only row: scaled up
+    x[1, 3:] = 0
+    x[2] = D.to_bf16_bits(np.full(K, 3e38, np.float32))
+    if M > 3 and K > 8:                       # tiny next to huge: underflows
+        x[3, :2] = D.to_bf16_bits(np.array([1e30, -1e-30], np.float32))
+    xd = dev_bf16(x)
+    out = (xd, Guarded((M, K), torch.int8), Guarded((M,), torch.float32)) \
+        if in_place else (Guarded((M, K), torch.bfloat16),
+                          Guarded((M, K), torch.int8),
+                          Guarded((M,), torch.float32))
+    y_t = out[0] if in_place else out[0].t
+    B.pow2_renorm_quantize(xd, out=(y_t, out[1].t, out[2].t))
+    torch.cuda.synchronize()
+    for g in out[1:] if in_place else out:
+        g.check()
+    y_ref = orc.pow2_renorm(x)
+    q_ref, s_ref = orc.quantize_act(y_ref)
+    assert np.array_equal(host_bf16(y_t), y_ref)
+    assert np.array_equal(out[1].t.cpu().numpy(), q_ref)
+    assert np.array_equal(out[2].t.cpu().numpy().view(np.uint32),
+                          s_ref.view(np.uint32))
+
+
 # ---------------------------------------------------------------------------
 # weight quantization, scale check, SwiGLU glue
 # ---------------------------------------------------------------------------
@@ -611,14 +643,21 @@ def test_chain_sampled_rows(orc, config, fused):
         projs = {p.name: BL.upload_proj(p, params[p.name]) for p in wl.projs}
         if fused:
             projs = BL.fuse_qkv(projs)
-        out = runner.run(xd, projs)
+        # as the benchmark chains the sweep with fused QKV: the block input
+        # after the first comes quantized from pow2_renorm_quantize
+        out = runner.run(xd, projs, x_quantized=fused and b > 0)
         ref = oracle_block_rows(orc, xr, params, wl.mlp, wl.o_input)
         torch.cuda.synchronize()
+        assert np.array_equal(runner.xq[0][ri].cpu().numpy(), ref["xq"]), b
         for n in ("q", "o", "fc1", "fc2"):
             assert np.array_equal(host_bf16(out[n][ri]), ref[n]), (b, n)
         if b == 0:
             nxt = bufs[0]
-            B.pow2_renorm(out["fc2"], out=nxt)
+            if fused:
+                B.pow2_renorm_quantize(out["fc2"], out=(nxt, runner.xq[0],
+                                                        runner.xs[0]))
+            else:
+                B.pow2_renorm(out["fc2"], out=nxt)
             torch.cuda.synchronize()
             xr = orc.pow2_renorm(ref["fc2"])
             assert np.array_equal(host_bf16(nxt[ri]), xr)

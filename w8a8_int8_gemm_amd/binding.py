@@ -39,6 +39,7 @@ SIGNATURES = {
     "w8a8_last_hip_error": (_I, []),
     "w8a8_silu_bf16": (_I, [_P, _P, _I64, _P]),
     "w8a8_pow2_renorm": (_I, [_P, _P, _I64, _I64, _P]),
+    "w8a8_pow2_renorm_quantize": (_I, [_P, _I64, _I64, _P, _P, _P, _P]),
     "w8a8_quantize_weight": (_I, [_P, _I64, _I64, _P, _P, _P]),
     "w8a8_check_scales": (_I, [_P, _I64, _P, _P]),
     "w8a8_swiglu_bf16": (_I, [_P, _P, _I64, _I64, _P]),
@@ -239,6 +240,27 @@ def pow2_renorm(x, *, out=None, stream=None):
     _check("w8a8_pow2_renorm", lib().w8a8_pow2_renorm(
         _ptr(x), _ptr(y), M, K, _stream(stream)))
     return y
+
+
+def pow2_renorm_quantize(x, *, out=None, stream=None):
+    """x: bf16 [M, K] -> (y bf16 [M, K], a_q int8 [M, K], a_scale float32
+    [M]): the power-of-two renormalization and the per-token quantization
+    of its result, in one pass."""
+    torch = _torch()
+    _need(x, torch.bfloat16, 2, "x")
+    M, K = x.shape
+    if out is None:
+        y = torch.empty_like(x)
+        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        s = torch.empty((M,), dtype=torch.float32, device=x.device)
+    else:
+        y, q, s = out
+        _need(y, torch.bfloat16, 2, "out[0]", (M, K))
+        _need(q, torch.int8, 2, "out[1]", (M, K))
+        _need(s, torch.float32, 1, "out[2]", (M,))
+    _check("w8a8_pow2_renorm_quantize", lib().w8a8_pow2_renorm_quantize(
+        _ptr(x), M, K, _ptr(y), _ptr(q), _ptr(s), _stream(stream)))
+    return y, q, s
 
 
 def quantize_weight(w, *, out=None, stream=None):

@@ -140,14 +140,19 @@ class BlockRunner:
                "fc1": self.xq[2], "fc2": self.hq}
         return {n: src[n] for n in projs}
 
-    def run(self, x, projs: dict, stream=None, on_gemm=None):
-        """x: bf16 [M, H].  Returns the dict of BF16 outputs."""
+    def run(self, x, projs: dict, stream=None, on_gemm=None,
+            x_quantized: bool = False):
+        """x: bf16 [M, H].  Returns the dict of BF16 outputs.  With
+        ``x_quantized`` the buffers ``xq[0]``, ``xs[0]`` already hold the
+        quantization of x (written together with x by
+        ``pow2_renorm_quantize`` between blocks) and Q, K and V use them."""
         def gemm(name, q, s):
             self._gemm(projs, name, q, s, stream, on_gemm)
 
         # Q, K, V: one shared quantization of the block input (and, fused,
         # one GEMM over the concatenated weights).
-        B.quantize_act(x, out=(self.xq[0], self.xs[0]), stream=stream)
+        if not x_quantized:
+            B.quantize_act(x, out=(self.xq[0], self.xs[0]), stream=stream)
         for n in (("qkv",) if "qkv" in projs else ("q", "k", "v")):
             gemm(n, self.xq[0], self.xs[0])
         # attention output projection and FC1 quantize their own inputs.

@@ -17,5 +17,8 @@ hipError_t launch_swiglu(const uint16_t *h, uint16_t *y, int64_t M, int64_t F,
                          hipStream_t stream);
 hipError_t launch_swiglu_quant(const uint16_t *h, int8_t *q, float *scale,
                                int64_t M, int64_t F, hipStream_t stream);
+hipError_t launch_pow2_renorm_quant(const uint16_t *x, uint16_t *y, int8_t *q,
+                                    float *sa, int64_t M, int64_t K,
+                                    hipStream_t stream);
 
 }  // namespace w8a8

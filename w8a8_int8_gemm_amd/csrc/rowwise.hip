@@ -40,7 +40,14 @@ constexpr int kThreads = 256;  // 4 waves of 64
 constexpr int kWaves = kThreads / 64;
 
 // OP_QUANT_W: per-output-channel weight rows; an all-zero row takes scale 1.
-enum RowOp : int { OP_QUANT = 0, OP_RENORM = 2, OP_QUANT_W = 3 };
+// OP_RENORM_QUANT: the power-of-two renormalization written to `aux`, and
+// the per-token quantization of that renormalized row, in one pass.
+enum RowOp : int {
+  OP_QUANT = 0,
+  OP_RENORM = 2,
+  OP_QUANT_W = 3,
+  OP_RENORM_QUANT = 4
+};
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -131,7 +138,7 @@ __device__ __forceinline__ uint32_t renorm_pair(uint32_t packed, int e) {
 template <int CH, int WPR, int OP>
 __global__ __launch_bounds__(kThreads) void row_kernel(
     const uint16_t *x, void *out, float *__restrict__ scale, int64_t M,
-    int K) {
+    int K, uint16_t *aux) {
   constexpr int RPB = kWaves / WPR;  // rows per block
   __shared__ float part_max[kWaves];
   const int lane = threadIdx.x & 63;
@@ -159,6 +166,42 @@ __global__ __launch_bounds__(kThreads) void row_kernel(
     amax = part_max[base];
 #pragma unroll
     for (int p = 1; p < WPR; ++p) amax = fmaxf(amax, part_max[base + p]);
+  }
+  if (OP == OP_RENORM_QUANT) {
+    // Renormalize in registers, then take the row maximum again from the
+    // renormalized BF16 values, so the codes and scale are exactly those a
+    // separate quantization of the written row computes.
+    int ex = 0;
+    frexpf(amax, &ex);
+    const int e = (amax == 0.0f) ? 0 : ex - 1;
+    us2 mag2 = us2{0, 0};
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      v4u c = v[i];  // masked chunks are zero and stay zero
+      c.x = renorm_pair(c.x, e);
+      c.y = renorm_pair(c.y, e);
+      c.z = renorm_pair(c.z, e);
+      c.w = renorm_pair(c.w, e);
+      v[i] = c;
+      mag2 = mag_max4(mag2, c);
+    }
+    amax = wave_max(mag_to_f32(mag2));
+    if (WPR > 1) {
+      __syncthreads();  // every wave has read the first exchange
+      if (lane == 0) part_max[wave] = amax;
+      __syncthreads();
+      const int base = (wave / WPR) * WPR;
+      amax = part_max[base];
+#pragma unroll
+      for (int p = 1; p < WPR; ++p) amax = fmaxf(amax, part_max[base + p]);
+    }
+    if (!row_ok) return;
+    v4u *yr = reinterpret_cast<v4u *>(aux + row * (int64_t)K);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int j = (i * WPR + part) * 64 + lane;
+      if (j < chunks) __builtin_nontemporal_store(v[i], yr + j);
+    }
   }
   if (!row_ok) return;
 
@@ -482,13 +525,13 @@ hipError_t launch_silu_quant(const uint16_t *x, int8_t *q, float *scale,
 // Chunk-per-lane counts that are instantiated, per waves-per-row.
 template <int WPR, int OP>
 hipError_t launch_rows(const uint16_t *x, void *out, float *scale, int64_t M,
-                       int K, int ch, hipStream_t stream) {
+                       int K, int ch, hipStream_t stream, uint16_t *aux) {
   constexpr int RPB = kWaves / WPR;
   const dim3 grid((unsigned)((M + RPB - 1) / RPB));
 #define W8A8_ROW_CASE(C)                                                  \
   if (ch <= C) {                                                          \
     hipLaunchKernelGGL((row_kernel<C, WPR, OP>), grid, dim3(kThreads), 0, \
-                       stream, x, out, scale, M, K);                      \
+                       stream, x, out, scale, M, K, aux);                 \
     return hipGetLastError();                                             \
   }
   W8A8_ROW_CASE(1)
@@ -510,14 +553,15 @@ hipError_t launch_rows(const uint16_t *x, void *out, float *scale, int64_t M,
 
 template <int OP>
 hipError_t launch_row_op(const uint16_t *x, void *out, float *scale,
-                         int64_t M, int64_t K, hipStream_t stream) {
+                         int64_t M, int64_t K, hipStream_t stream,
+                         uint16_t *aux = nullptr) {
   const int chunks = (int)(K / 8);
   if (chunks <= 11 * 64) {
     const int ch = (chunks + 63) / 64;
-    return launch_rows<1, OP>(x, out, scale, M, (int)K, ch, stream);
+    return launch_rows<1, OP>(x, out, scale, M, (int)K, ch, stream, aux);
   }
   const int ch = (chunks + 4 * 64 - 1) / (4 * 64);
-  return launch_rows<4, OP>(x, out, scale, M, (int)K, ch, stream);
+  return launch_rows<4, OP>(x, out, scale, M, (int)K, ch, stream, aux);
 }
 
 }  // namespace
@@ -550,6 +594,12 @@ hipError_t launch_silu(const uint16_t *x, uint16_t *y, int64_t n,
 hipError_t launch_quantize_weight(const uint16_t *w, int8_t *q, float *sw,
                                   int64_t N, int64_t K, hipStream_t stream) {
   return launch_row_op<OP_QUANT_W>(w, q, sw, N, K, stream);
+}
+
+hipError_t launch_pow2_renorm_quant(const uint16_t *x, uint16_t *y, int8_t *q,
+                                    float *sa, int64_t M, int64_t K,
+                                    hipStream_t stream) {
+  return launch_row_op<OP_RENORM_QUANT>(x, q, sa, M, K, stream, y);
 }
 
 hipError_t launch_check_scales(const float *sw, int64_t N, int *bad,

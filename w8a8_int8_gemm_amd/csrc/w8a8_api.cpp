@@ -318,4 +318,24 @@ int w8a8_pow2_renorm(const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                                               static_cast<hipStream_t>(stream)));
 }
 
+int w8a8_pow2_renorm_quantize(const uint16_t *x, int64_t M, int64_t K,
+                              uint16_t *y, int8_t *a_q, float *a_scale,
+                              void *stream) {
+  if (!x || !y || !a_q || !a_scale) return W8A8_ERR_NULL;
+  if (M < 1 || M > kMaxTokenRows || K < 8 || K % 8 != 0 || K > kQuantMaxK)
+    return W8A8_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(a_q, 8) ||
+      !aligned(a_scale, 4))
+    return W8A8_ERR_ALIGN;
+  const Range rx = range_of(x, M * K * 2), ry = range_of(y, M * K * 2),
+              rq = range_of(a_q, M * K), rs = range_of(a_scale, M * 4);
+  if ((x != y && overlap(rx, ry)) || overlap(rx, rq) || overlap(rx, rs) ||
+      overlap(ry, rq) || overlap(ry, rs) || overlap(rq, rs))
+    return W8A8_ERR_ALIAS;
+  int st = check_device();
+  if (st != W8A8_OK) return st;
+  return hip_status(w8a8::launch_pow2_renorm_quant(
+      x, y, a_q, a_scale, M, K, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"
