@@ -12,8 +12,13 @@
 //
 // Design (gfx950):
 //   * Block tile BM tokens x BN channels, K staged BK bytes at a time through
-//     LDS, double buffered.  Tiles are filled with global_load_lds_dwordx4
+//     LDS, double buffered.  Tiles are filled with buffer_load_dwordx4 ... lds
 //     (direct global -> LDS, 16 bytes per lane), so staging costs no VGPRs.
+//     The buffer form, through one buffer resource per operand tile, rather
+//     than the global form: the compiler treats an outstanding global (flat)
+//     load into LDS as touching both memory and LDS and then waits for every
+//     LDS read (lgkmcnt(0)) before each use of a fragment; with buffer loads
+//     its fragment waits count only the reads a k-step still needs.
 //   * LDS rows are BK bytes; the 16-byte chunk c of row r sits at position
 //     c ^ swz(r), which makes the wave's 16-byte fragment reads free of bank
 //     conflicts whether the LDS serves 8 lanes x 16 B (32 banks) or
@@ -47,7 +52,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void gbl_void;
 
 constexpr int kXcds = 8;
 constexpr int EPI_PARTIAL = 3;       // split-K slice: raw INT32, [M,N] layout
@@ -102,8 +106,24 @@ __device__ __forceinline__ int swz(int r, int c) {
   return c ^ (((r >> 1) ^ ((r & 1) << 2)) & 7);
 }
 
-__device__ __forceinline__ void load_lds16(const int8_t *g, lds_void *l) {
-  __builtin_amdgcn_global_load_lds((gbl_void *)g, l, 16, 0, 0);
+// 16 bytes per lane from buffer `r` at byte voff + soff into LDS at `l`
+// (lane i's bytes at l + 16 i).
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, int voff,
+                                           int soff, lds_void *l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voff, soff, 0, 0);
+}
+
+// A raw buffer resource (no stride, no swizzle) over [base, base + 2^31 - 1)
+// bytes.  The address is first made wave-uniform: readfirstlane returns a
+// signed int, so each 32-bit half is widened through uint32_t (a sign
+// extension of the low half would corrupt the high half).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const int8_t *base) {
+  const uint64_t ad = (uint64_t)(uintptr_t)base;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ad);
+  const uint64_t hi =
+      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ad >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)((hi << 32) | lo),
+                                           (short)0, 0x7fffffff, 0x00020000);
 }
 
 __device__ __forceinline__ v4i read_lds16(const int8_t *lds_base, int off) {
@@ -207,8 +227,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(KernelArgs p) {
   // Direct loads: a uniform base per operand, advanced by BK bytes per
   // stage, plus a 32-bit per-lane offset per load instruction (the row in
   // the tile, clamped to the last valid row, times K, plus the chunk that
-  // lands in this lane's 16 LDS bytes).  Row offsets stay below
-  // 256 * W8A8_MAX_K < 2^31.
+  // lands in this lane's 16 LDS bytes).  Row offsets plus the stage offset
+  // stay below 257 * W8A8_MAX_K, far inside the 2^31 - 1 bytes of the
+  // buffer resource below.
   const int8_t *a_base = p.a + (int64_t)m0 * p.K + (int64_t)kt0 * C::BK;
   const int8_t *b_base = p.w + (int64_t)n0 * p.K + (int64_t)kt0 * C::BK;
   int oa[C::A_LOADS], ob[C::B_LOADS];
@@ -227,20 +248,23 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(KernelArgs p) {
     ob[j] = min(r, p.N - 1 - n0) * p.K + c * 16;
   }
 
+  // One buffer resource per operand over this tile's rows; a load's byte
+  // offset is its lane offset above plus the stage's BK * src.
+  const auto ra = tile_rsrc(a_base);
+  const auto rb = tile_rsrc(b_base);
+
   // Request stage `src` of this split into ring slot `slot`.
   auto issue_into = [&](int slot, int src) {
-    const int stage_idx = src;
+    const int soff = __builtin_amdgcn_readfirstlane(src * C::BK);
     int8_t *sa_base = smem + slot * C::STAGE;
     int8_t *sb_base = sa_base + C::A_BYTES;
-    const int8_t *ga = a_base + (int64_t)stage_idx * C::BK;
-    const int8_t *gb = b_base + (int64_t)stage_idx * C::BK;
 #pragma unroll
     for (int j = 0; j < C::A_LOADS; ++j)
-      load_lds16(ga + oa[j],
+      load_lds16(ra, oa[j], soff,
                  (lds_void *)(sa_base + (j * C::WAVES + wave) * 1024));
 #pragma unroll
     for (int j = 0; j < C::B_LOADS; ++j)
-      load_lds16(gb + ob[j],
+      load_lds16(rb, ob[j], soff,
                  (lds_void *)(sb_base + (j * C::WAVES + wave) * 1024));
   };
 
