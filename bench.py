@@ -186,7 +186,7 @@ def main():
         qbuf = torch.empty((M, p0.K), dtype=torch.int8, device=dev)
         sbuf = torch.empty((M,), dtype=torch.float32, device=dev)
         ybuf = torch.empty((M, p0.N), dtype=torch.bfloat16, device=dev)
-        wsb = torch.empty((max(B.workspace_bytes(M, p0.N, p0.K), 256),),
+        wsb = torch.empty((max(B.gemm_workspace_bytes(M, p0.N, p0.K), 256),),
                           dtype=torch.uint8, device=dev)
 
     ops_per_step = 0

@@ -74,11 +74,11 @@ typedef enum {
  * [-127, 127].  A row of zeros gives a_scale = 0 and zero codes.  FP32
  * subnormals are kept.
  * Shape: 1 <= M <= 2^24 - 1 (a launch holds fewer than 2^32 work-items,
- * up to 256 per row), 8 <= K <= 90112 and K % 8 == 0 (16-byte rows of
- * BF16; a row stays in registers, 44 chunks per lane); rows whose
- * length is not a multiple of the kernel's chunk width are handled by
- * masking the partial chunk, as the LightX2V page's quantizer does
- * (commit notes, "Changes" table).
+ * up to 256 per row), 8 <= K <= W8A8_MAX_K and K % 8 == 0 (16-byte rows
+ * of BF16; up to K = 90112 a row stays in registers and is read once,
+ * longer rows are read twice); rows whose length is not a multiple of the
+ * kernel's chunk width are handled by masking the partial chunk, as the
+ * LightX2V page's quantizer does (commit notes, "Changes" table).
  * Errors: NULL, SHAPE, ALIGN, ALIAS (a_q or a_scale overlapping x or each
  * other), DEVICE, HIP.
  */
@@ -91,13 +91,18 @@ int w8a8_quantize_act(const uint16_t *x, int64_t M, int64_t K, int8_t *a_q,
  *   a_scale   FP32 [M] per-token scales, 4-byte aligned.
  *   w_q       INT8 [N,K] weights in a Linear's stored layout (one row per
  *             output channel), 16-byte aligned, consumed as stored.
- *   w_scale   FP32 [N] per-output-channel scales (finite, > 0), 16-byte
- *             aligned.
- *   bias      BF16 [N] or NULL (no bias), 8-byte aligned.
+ *   w_scale   FP32 [N] per-output-channel scales (finite, > 0), 4-byte
+ *             aligned (16-byte alignment lets the epilogue use vector
+ *             loads; a channel slice of a larger array is accepted).
+ *   bias      BF16 [N] or NULL (no bias), 2-byte aligned (8-byte: vector
+ *             loads).
  *   out       [M,N] of the type selected by out_dtype, 16-byte aligned.
  *   out_dtype W8A8_OUT_BF16, W8A8_OUT_FP32 or W8A8_OUT_I32.
- *   workspace device scratch of at least w8a8_workspace_bytes(M, N, K)
- *             bytes (may be NULL when that is 0), 256-byte aligned.
+ *   workspace device scratch of at least w8a8_gemm_workspace_bytes(M, N,
+ *             K) bytes (w8a8_workspace_bytes is always enough; may be NULL
+ *             when the former is 0), 16-byte aligned.  It holds INT32
+ *             partial sums of split-K launches; its contents before and
+ *             after the call do not matter.
  * acc[m,n] = sum_k a_q[m,k] * w_q[n,k] exactly in INT32;
  * t = ((float)acc * a_scale[m]) * w_scale[n] + bf16->f32(bias[n]), each
  * operation rounded in binary32 with no fused multiply-add; BF16 output is
@@ -117,13 +122,20 @@ int w8a8_gemm(const int8_t *a_q, const float *a_scale, const int8_t *w_q,
               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Whole projection: w8a8_quantize_act of x into the workspace, then
- * w8a8_gemm with BF16 output.  y = bf16(((float)acc*sa[m])*sw[n] + bias[n]).
+ * Whole projection, the quantized Linear that replaces a BF16 Linear on
+ * each of the six block projections ("feat(mps): support MiniMax-H3 INT8
+ * inference on Apple M5", LightX2V pull request #1672, description: W8A8
+ * on Q, K, V, attention output, FC1 and FC2; commit notes: per-token
+ * activation quantization feeding the INT8 GEMM at native K): per-token
+ * quantization of x (as w8a8_quantize_act) into the workspace, then the
+ * INT8 GEMM with BF16 output (as w8a8_gemm), y = bf16(((float)acc*sa[m]) *
+ * sw[n] + bias[n]) with the bias added before the one rounding ("MLX
+ * implementation and experiment report", "What the default preserves").
  *   x   BF16 [M,K] (16-byte aligned); y BF16 [M,N] (16-byte aligned);
  *   the other arguments as for w8a8_gemm.
- * Workspace: at least w8a8_linear_workspace_bytes(M, N, K) bytes, 256-byte
- * aligned, not overlapping any argument.  K <= 90112 and M <= 2^24 - 1 (the
- * quantizer's bounds).
+ * Workspace: at least w8a8_workspace_bytes(M, N, K) bytes, 16-byte
+ * aligned, not overlapping any argument (the INT8 codes, their scales and
+ * the GEMM's partial sums).  M <= 2^24 - 1 (the quantizer's bound).
  * Errors: as w8a8_gemm.
  */
 int w8a8_linear(const uint16_t *x, const int8_t *w_q, const float *w_scale,
@@ -156,13 +168,16 @@ int w8a8_quantize_weight(const uint16_t *w, int64_t N, int64_t K,
 int w8a8_check_scales(const float *w_scale, int64_t N, int32_t *bad_count,
                       void *stream);
 
-/* Workspace bytes w8a8_gemm needs for this shape (0 when none); 0 as well
- * for shapes the contract rejects. */
+/* Workspace bytes that serve both w8a8_linear and w8a8_gemm for this
+ * shape: the INT8 activation codes [M,K] and their scales [M] that
+ * w8a8_linear stages, plus the INT32 split-K partial sums of the GEMM, each
+ * part starting at a 256-byte offset.  0 for shapes the contract rejects. */
 size_t w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
-/* Workspace bytes w8a8_linear needs: quantized activations, their scales
- * and w8a8_gemm's own workspace, each 256-byte aligned. */
-size_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+/* The smaller workspace w8a8_gemm alone needs (only its split-K partial
+ * sums; 0 when the plan for this shape splits nothing, and for shapes the
+ * contract rejects). */
+size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Static description of a status code (never NULL). */
 const char *w8a8_status_string(int status);
@@ -170,6 +185,11 @@ const char *w8a8_status_string(int status);
 /* hipError_t code of the last W8A8_ERR_HIP returned on this thread (0 if
  * none yet), for diagnostics. */
 int w8a8_last_hip_error(void);
+
+/* SHA-256 (64 hex digits) of the sources this library was compiled from
+ * (its kernels, API layer and this header), so a caller can refuse a build
+ * that no longer matches the sources beside it. */
+const char *w8a8_build_id(void);
 
 /*
  * Glue between projections (not part of the W8A8 method; it produces the
@@ -204,7 +224,8 @@ int w8a8_last_hip_error(void);
  * w8a8_quantize_act_silu: w8a8_silu_bf16 followed by w8a8_quantize_act in
  *   one pass over x (the SiLU values are rounded to BF16 before they are
  *   quantized, exactly as the two separate calls do); the BF16 SiLU output
- *   is not written.  Arguments and errors as w8a8_quantize_act.
+ *   is not written.  Arguments and errors as w8a8_quantize_act, with
+ *   8 <= K <= 90112.
  */
 int w8a8_silu_bf16(const uint16_t *x, uint16_t *y, int64_t n, void *stream);
 

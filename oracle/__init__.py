@@ -16,12 +16,16 @@ the default build ``oracle/libw8a8_oracle.so``.
 from __future__ import annotations
 
 import ctypes
+import os
 from pathlib import Path
 
 import numpy as np
 
 _HERE = Path(__file__).resolve().parent
-LIB_PATH = _HERE / "libw8a8_oracle.so"
+# W8A8_ORACLE_LIB names another build of the same source (the sanitizer
+# test runs the pins against a -fsanitize=undefined build this way).
+LIB_PATH = Path(os.environ.get("W8A8_ORACLE_LIB",
+                               _HERE / "libw8a8_oracle.so"))
 
 _ERRORS = {
     1: "NULL pointer",

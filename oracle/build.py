@@ -7,6 +7,7 @@ any x86-64 host it is copied to.
 """
 from __future__ import annotations
 
+import os
 import subprocess
 from pathlib import Path
 
@@ -21,10 +22,17 @@ CFLAGS = [
 ]
 
 
+def extra_cflags() -> list[str]:
+    """Flags added to every oracle build from W8A8_ORACLE_CFLAGS (the
+    sanitizer test builds its copies with -fsanitize=undefined)."""
+    return os.environ.get("W8A8_ORACLE_CFLAGS", "").split()
+
+
 def build_from(src: Path, out: Path) -> Path:
     """Compile one oracle source file into a shared object."""
     tmp = out.with_suffix(".so.tmp")
-    cmd = ["gcc", *CFLAGS, "-I", str(HERE), "-o", str(tmp), str(src), "-lm"]
+    cmd = ["gcc", *CFLAGS, *extra_cflags(), "-I", str(HERE), "-o", str(tmp),
+           str(src), "-lm"]
     subprocess.run(cmd, check=True)
     tmp.replace(out)
     return out

@@ -91,8 +91,8 @@ def linear(**kw):
     (dict(M=(1 << 31) - 1, N=21504, wsb=1 << 62), SHAPE),
     (dict(dt=3), OUT_DTYPE), (dict(dt=-1), OUT_DTYPE),
     (dict(aq=BUF["aq"] + 8), ALIGN), (dict(w=BUF["w"] + 4), ALIGN),
-    (dict(out=BUF["out"] + 2), ALIGN), (dict(sw=BUF["sw"] + 4), ALIGN),
-    (dict(sa=BUF["sa"] + 2), ALIGN), (dict(bias=BUF["bias"] + 2), ALIGN),
+    (dict(out=BUF["out"] + 2), ALIGN), (dict(sw=BUF["sw"] + 2), ALIGN),
+    (dict(sa=BUF["sa"] + 2), ALIGN), (dict(bias=BUF["bias"] + 1), ALIGN),
     (dict(out=BUF["aq"]), ALIAS), (dict(out=BUF["w"] + 1024), ALIAS),
     (dict(out=BUF["sw"] - 16), ALIAS), (dict(out=BUF["bias"]), ALIAS),
 ])
@@ -102,12 +102,29 @@ def test_gemm_rejects(kw, code):
 
 def test_gemm_workspace_checks():
     # M = 64 plans split-K and needs a workspace
-    need = B.workspace_bytes(64, 5376, 5376)
+    need = B.gemm_workspace_bytes(64, 5376, 5376)
     assert need > 0
     assert gemm(M=64, N=5376, K=5376, ws=None, wsb=0) == WORKSPACE
     assert gemm(M=64, N=5376, K=5376, wsb=need - 1) == WORKSPACE
-    assert gemm(M=64, N=5376, K=5376, ws=BUF["ws"] + 16, wsb=need) == ALIGN
+    assert gemm(M=64, N=5376, K=5376, ws=BUF["ws"] + 8, wsb=need) == ALIGN
     assert gemm(M=64, N=5376, K=5376, ws=BUF["out"], wsb=need) == ALIAS
+
+
+def test_gemm_accepts_planned_alignments():
+    """Scales need only 4-byte alignment, the bias 2-byte and the workspace
+    16-byte (a channel slice of larger arrays): such calls pass validation
+    and reach the device check (no device here)."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present")
+    assert gemm(sw=BUF["sw"] + 4, bias=BUF["bias"] + 2) == DEVICE
+    assert gemm(M=64, N=5376, K=5376, ws=BUF["ws"] + 16,
+                wsb=B.gemm_workspace_bytes(64, 5376, 5376)) == DEVICE
+    assert linear(sw=BUF["sw"] + 12, bias=BUF["bias"] + 6,
+                  ws=BUF["ws"] + 16) == DEVICE
+    # K up to the INT32 bound through linear (the quantizer takes it too)
+    assert linear(M=3, N=256, K=B.MAX_K) == DEVICE
+    assert quant(K=B.MAX_K) == DEVICE
 
 
 def test_workspace_sizes():
@@ -116,25 +133,32 @@ def test_workspace_sizes():
     # into INT32 tiles of its own when s >= 2 (each slice at least 512
     # bytes of K, four 128-byte stages).
     tile = 256 * 256 * 4
-    assert B.workspace_bytes(4096, 4096, 5376) == 0           # 256 tiles
-    assert B.workspace_bytes(19077, 21504, 5376) == 0         # 6300: s = 1
-    assert B.workspace_bytes(19077, 5376, 5376) == 6 * 39 * tile   # 1575
-    assert B.workspace_bytes(37503, 5376, 21504) == 17 * 15 * tile  # 3087
-    assert B.workspace_bytes(4097, 4096, 1664) == 3 * 16 * tile    # 13 stages
-    assert B.workspace_bytes(4097, 4096, 1024) == 2 * 16 * tile
-    assert B.workspace_bytes(4097, 4096, 512) == 0            # 4 stages
-    ws = B.workspace_bytes(64, 5376, 5376)
+    g = B.gemm_workspace_bytes
+    assert g(4096, 4096, 5376) == 0           # 256 tiles
+    assert g(19077, 21504, 5376) == 0         # 6300: s = 1
+    assert g(19077, 5376, 5376) == 6 * 39 * tile   # 1575
+    assert g(37503, 5376, 21504) == 17 * 15 * tile  # 3087
+    assert g(4097, 4096, 1664) == 3 * 16 * tile    # 13 stages
+    assert g(4097, 4096, 1024) == 2 * 16 * tile
+    assert g(4097, 4096, 512) == 0            # 4 stages
+    ws = g(64, 5376, 5376)
     assert ws % (64 * 5376 * 4) == 0 and ws // (64 * 5376 * 4) >= 2
-    assert B.workspace_bytes(64, 100, 5376) == 0  # rejected shape
-    lw = B.linear_workspace_bytes(19077, 5376, 5376)
-    assert lw >= 19077 * 5376 + 19077 * 4 and lw % 256 == 0
+    assert g(64, 100, 5376) == 0  # rejected shape
+    # w8a8_workspace_bytes: the codes and scales linear stages, each at a
+    # 256-byte offset, plus the GEMM's partial sums (so it serves both)
+    r = lambda v: (v + 255) // 256 * 256
+    for M, N, K in [(19077, 5376, 5376), (64, 5376, 5376), (300, 384, 640),
+                    (3, 256, B.MAX_K)]:
+        assert B.workspace_bytes(M, N, K) == r(M * K) + r(4 * M) + g(M, N, K)
+    assert B.workspace_bytes(64, 100, 5376) == 0
+    assert B.workspace_bytes(1 << 24, 128, 128) == 0  # beyond the quantizer
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(x=None), NULL), (dict(q=None), NULL), (dict(s=None), NULL),
     (dict(M=0), SHAPE), (dict(M=1 << 24), SHAPE),
     (dict(K=4), SHAPE), (dict(K=5377), SHAPE),
-    (dict(K=B.QUANT_MAX_K + 8), SHAPE),
+    (dict(K=B.MAX_K + 8), SHAPE),
     (dict(x=BUF["x"] + 8), ALIGN), (dict(q=BUF["aq"] + 4), ALIGN),
     (dict(s=BUF["sa"] + 1), ALIGN),
     (dict(q=BUF["x"] + 16), ALIAS), (dict(s=BUF["aq"] + 64), ALIAS),
@@ -145,8 +169,9 @@ def test_quantize_rejects(kw, code):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(x=None), NULL), (dict(y=None), NULL), (dict(M=0), SHAPE),
-    (dict(K=B.QUANT_MAX_K + 128), SHAPE), (dict(ws=None), WORKSPACE),
-    (dict(wsb=100), WORKSPACE), (dict(ws=BUF["ws"] + 128), ALIGN),
+    (dict(K=B.MAX_K + 128), SHAPE), (dict(ws=None), WORKSPACE),
+    (dict(wsb=100), WORKSPACE), (dict(ws=BUF["ws"] + 8), ALIGN),
+    (dict(sw=BUF["sw"] + 2), ALIGN), (dict(bias=BUF["bias"] + 1), ALIGN),
     (dict(x=BUF["x"] + 2), ALIGN), (dict(y=BUF["x"]), ALIAS),
     (dict(ws=BUF["w"]), ALIAS),
 ])
@@ -164,6 +189,8 @@ def test_glue_rejects():
     assert lib.w8a8_pow2_renorm(BUF["x"], BUF["x"] + 16, 4, 64, None) == ALIAS
     assert lib.w8a8_quantize_act_silu(BUF["x"], 4, 12, BUF["aq"], BUF["sa"],
                                       None) == SHAPE
+    assert lib.w8a8_quantize_act_silu(BUF["x"], 4, B.GLUE_MAX_K + 8,
+                                      BUF["aq"], BUF["sa"], None) == SHAPE
 
 
 def test_weight_and_gated_glue_reject():
@@ -172,7 +199,7 @@ def test_weight_and_gated_glue_reject():
     assert qw(None, 4, 64, BUF["aq"], BUF["sa"], None) == NULL
     assert qw(BUF["w"], 0, 64, BUF["aq"], BUF["sa"], None) == SHAPE
     assert qw(BUF["w"], 4, 60, BUF["aq"], BUF["sa"], None) == SHAPE
-    assert qw(BUF["w"], 4, B.QUANT_MAX_K + 8, BUF["aq"], BUF["sa"],
+    assert qw(BUF["w"], 4, B.MAX_K + 8, BUF["aq"], BUF["sa"],
               None) == SHAPE
     assert qw(BUF["w"] + 8, 4, 64, BUF["aq"], BUF["sa"], None) == ALIGN
     assert qw(BUF["w"], 4, 64, BUF["w"] + 256, BUF["sa"], None) == ALIAS
@@ -190,7 +217,7 @@ def test_weight_and_gated_glue_reject():
     assert sg(BUF["x"], BUF["x"] + 256, 2, 64, None) == ALIAS
     qs = lib.w8a8_quantize_act_swiglu
     assert qs(BUF["x"], 2, 64, None, BUF["sa"], None) == NULL
-    assert qs(BUF["x"], 2, B.QUANT_MAX_K + 8, BUF["aq"], BUF["sa"],
+    assert qs(BUF["x"], 2, B.GLUE_MAX_K + 8, BUF["aq"], BUF["sa"],
               None) == SHAPE
     assert qs(BUF["x"], 2, 64, BUF["aq"] + 4, BUF["sa"], None) == ALIGN
     assert qs(BUF["x"], 2, 64, BUF["x"] + 128, BUF["sa"], None) == ALIAS
@@ -205,7 +232,7 @@ def test_renorm_quantize_rejects():
     assert rq(x, 4, 64, y, q, None, None) == NULL
     assert rq(x, 0, 64, y, q, sa, None) == SHAPE
     assert rq(x, 4, 60, y, q, sa, None) == SHAPE
-    assert rq(x, 4, B.QUANT_MAX_K + 8, y, q, sa, None) == SHAPE
+    assert rq(x, 4, B.GLUE_MAX_K + 8, y, q, sa, None) == SHAPE
     assert rq(x + 8, 4, 64, y, q, sa, None) == ALIGN
     assert rq(x, 4, 64, y + 8, q, sa, None) == ALIGN
     assert rq(x, 4, 64, y, q + 4, sa, None) == ALIGN
@@ -231,6 +258,19 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(B, "LIB_PATH", tmp_path / "missing.so")
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(ImportError):
+        B.lib()
+
+
+def test_build_id_matches_sources(monkeypatch):
+    """The library reports the SHA-256 of the sources it was built from;
+    the binding refuses to load a build whose sources have changed since."""
+    lib = B.lib()
+    assert lib.w8a8_build_id().decode() == B._expected_build_id()
+    assert not B.build_is_stale()
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "_expected_build_id", lambda: "0" * 64)
+    assert B.build_is_stale()
+    with pytest.raises(ImportError, match="other sources"):
         B.lib()
 
 

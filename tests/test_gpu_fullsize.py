@@ -1,0 +1,169 @@
+"""Parity with the oracle at the DiT workloads' full sizes, in the launch
+sequence the benchmark times (one block's kernels through BlockRunner,
+with Q, K and V fused into one GEMM where the benchmark fuses them).
+
+* 4096 tokens, one block: every output element of all six projections,
+  the codes and scales of the block input and of FC2's input.
+* 19077 and 37503 tokens, one block (and the pages' H3 shapes at 19077):
+  one token row from every 256-token tile (the large GEMM tiles), at an
+  offset that changes from tile to tile, plus the first and last rows;
+  each row is compared over every output channel of every projection.
+* The 50-block chains at 19077 tokens, stage by stage: before every block
+  the test reads some rows of the block input the device holds; the oracle
+  takes those rows through the block, and the device's codes, scales and
+  all six outputs must equal the oracle's bit for bit; the device's
+  renormalized FC2 rows (the next block's input) must equal the oracle's
+  renormalization of the device's FC2 rows.
+
+All comparisons are bit-exact (INT8 codes, FP32 scales, BF16 outputs).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from tests.blockref import block_rows, spread_rows, tile_rows
+from w8a8_int8_gemm_amd import binding as B
+from w8a8_int8_gemm_amd import block as BL
+from w8a8_int8_gemm_amd import datagen as D
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+THREADS = 16  # host threads for drawing a block's weights
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def host_bf16(t):
+    return BL.from_device_bf16(t)
+
+
+def upload(wl, params, fused):
+    projs = {p.name: BL.upload_proj(p, params[p.name]) for p in wl.projs}
+    return BL.fuse_qkv(projs) if fused else projs
+
+
+def compare_block(runner, out, ref, ri, where, o_input="x", full=False):
+    """Device rows `ri` (all rows when `full`) of a block run against the
+    oracle's `ref` for the same rows."""
+    sel = (lambda t: t) if full else (lambda t: t[ri])
+
+    def same(name, got, want):
+        if got.dtype == np.float32:
+            got, want = got.view(np.uint32), want.view(np.uint32)
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, (f"{where}: {name}: {len(bad)} of {got.size} "
+                               f"differ, first {bad[:4].tolist()}")
+
+    same("block input codes", sel(runner.xq[0]).cpu().numpy(), ref["xq"])
+    same("block input scales", sel(runner.xs[0]).cpu().numpy(), ref["xs"])
+    # the attention output projection (when it reads X) and FC1 quantize
+    # the block input again, each into its own buffer
+    for i in ((1, 2) if o_input == "x" else (2,)):
+        same(f"block input codes ({i})", sel(runner.xq[i]).cpu().numpy(),
+             ref["xq"])
+        same(f"block input scales ({i})", sel(runner.xs[i]).cpu().numpy(),
+             ref["xs"])
+    if o_input == "v":
+        same("O input codes", sel(runner.oq).cpu().numpy(), ref["oq"])
+        same("O input scales", sel(runner.xs[1]).cpu().numpy(), ref["os"])
+    for n in ("q", "k", "v", "o", "fc1", "fc2"):
+        same(n, host_bf16(sel(out[n])), ref[n])
+    same("FC2 input codes", sel(runner.hq).cpu().numpy(), ref["hq"])
+    same("FC2 input scales", sel(runner.hs).cpu().numpy(), ref["hs"])
+
+
+# ---------------------------------------------------------------------------
+# 4096 tokens: every output
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def block4096(orc):
+    wl = D.WORKLOADS[1]
+    say(f"oracle of {wl.name}: all {wl.M} rows of the six projections")
+    params = D.block_params(wl, 0, threads=THREADS)
+    x = D.activations(wl.M, D.HIDDEN, wl.seed)
+    return wl, params, x, block_rows(orc, x, params, wl.mlp, wl.o_input)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_block_m4096_every_output(block4096, fused):
+    wl, params, x, ref = block4096
+    say(f"{wl.name} M={wl.M}, fused QKV {fused}: every output element")
+    runner = BL.BlockRunner(wl.M, fused_qkv=fused, projs=wl.projs,
+                            mlp=wl.mlp, o_input=wl.o_input)
+    out = runner.run(BL.to_device_bf16(x), upload(wl, params, fused))
+    torch.cuda.synchronize()
+    compare_block(runner, out, ref, None, wl.name, wl.o_input, full=True)
+
+
+# ---------------------------------------------------------------------------
+# 19077 / 37503 tokens: a row from every token tile
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("config,fused", [(2, True), (2, False), (3, True),
+                                          (3, False), (5, False)])
+def test_block_row_per_token_tile(orc, config, fused):
+    wl = D.WORKLOADS[config]
+    rows = tile_rows(wl.M, 256, salt=config)
+    say(f"{wl.name} M={wl.M}, fused QKV {fused}: {len(rows)} rows, one per "
+        "256-token tile")
+    params = D.block_params(wl, 0, threads=THREADS)
+    x = D.activations(wl.M, D.HIDDEN, wl.seed)
+    runner = BL.BlockRunner(wl.M, fused_qkv=fused, projs=wl.projs,
+                            mlp=wl.mlp, o_input=wl.o_input)
+    out = runner.run(BL.to_device_bf16(x), upload(wl, params, fused))
+    torch.cuda.synchronize()
+    ref = block_rows(orc, x[rows], params, wl.mlp, wl.o_input)
+    compare_block(runner, out, ref, torch.from_numpy(rows).cuda(), wl.name,
+                  wl.o_input)
+
+
+# ---------------------------------------------------------------------------
+# the 50-block chains, stage by stage
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("config,fused,nrows", [(4, True, 64),
+                                                (6, False, 16)])
+def test_chain_every_block_stagewise(orc, config, fused, nrows):
+    wl = D.WORKLOADS[config]
+    rows = spread_rows(wl.M, nrows, salt=config)
+    ri = torch.from_numpy(rows).cuda()
+    say(f"{wl.name} M={wl.M}: all {wl.blocks} blocks stage by stage on "
+        f"{len(rows)} rows, fused QKV {fused}")
+    x = D.activations(wl.M, D.HIDDEN, wl.seed)
+    xd = BL.to_device_bf16(x)
+    runner = BL.BlockRunner(wl.M, fused_qkv=fused, projs=wl.projs,
+                            mlp=wl.mlp, o_input=wl.o_input)
+    bufs = [torch.empty_like(xd), torch.empty_like(xd)]
+    xr = x[rows]  # rows of the block input, as the device holds them
+    for b in range(wl.blocks):
+        params = D.block_params(wl, b, threads=THREADS)
+        projs = upload(wl, params, fused)
+        # as the benchmark chains the blocks with fused QKV: after the first
+        # block the input comes quantized from pow2_renorm_quantize
+        out = runner.run(xd, projs, x_quantized=fused and b > 0)
+        torch.cuda.synchronize()
+        ref = block_rows(orc, xr, params, wl.mlp, wl.o_input)
+        compare_block(runner, out, ref, ri, f"block {b}", wl.o_input)
+        if b + 1 < wl.blocks:
+            nxt = bufs[b % 2]
+            if fused:
+                B.pow2_renorm_quantize(out["fc2"], out=(nxt, runner.xq[0],
+                                                        runner.xs[0]))
+            else:
+                B.pow2_renorm(out["fc2"], out=nxt)
+            torch.cuda.synchronize()
+            got = host_bf16(nxt[ri])
+            want = orc.pow2_renorm(host_bf16(out["fc2"][ri]))
+            assert np.array_equal(got, want), f"renormalized input {b + 1}"
+            xr, xd = got, nxt
+        del projs, params
+        if b % 10 == 9:
+            say(f"  blocks 0-{b} bit-exact")

@@ -87,10 +87,12 @@ def edge_rows(K: int) -> np.ndarray:
 # quantization, SiLU, renormalization
 # ---------------------------------------------------------------------------
 
-# The M = 5000 and M = 4500 cases span thousands of work groups.
+# The M = 5000 and M = 4500 cases span thousands of work groups; K above
+# 90112 takes the two-pass kernel for long rows, up to the INT32 bound.
 QUANT_SHAPES = [(1, 8), (3, 128), (65, 5376), (64, 5632), (5, 5640),
                 (7, 21504), (2, 90112), (257, 384), (33, 1000),
-                (5000, 5376), (4500, 1000)]
+                (5000, 5376), (4500, 1000), (6, 90120), (7, 130944),
+                (300, 98304)]
 
 
 @pytest.mark.parametrize("M,K", QUANT_SHAPES)
@@ -202,6 +204,7 @@ def test_pow2_renorm_quantize(orc, M, K, in_place):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("N,K", [(5376, 5376), (300, 21504), (7, 8),
+                                 (9, 130944),
                                  (1000, 14336)])
 def test_quantize_weight(orc, N, K):
     say(f"quantize_weight N={N} K={K}")
@@ -303,7 +306,7 @@ def gemm_inputs(M, N, K, seed):
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
 def test_gemm_i32(orc, M, N, K):
-    say(f"gemm I32 M={M} N={N} K={K} workspace={B.workspace_bytes(M, N, K)}")
+    say(f"gemm I32 M={M} N={N} K={K} workspace={B.gemm_workspace_bytes(M, N, K)}")
     a, w, sa, sw, bias = gemm_inputs(M, N, K, 1)
     og = Guarded((M, N), torch.int32)
     B.gemm(dev(a), dev(sa), dev(w), dev(sw), dev_bf16(bias),
@@ -346,7 +349,8 @@ def test_gemm_fp32_bf16(orc, M, N, K, with_bias):
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 5376, 5376), (129, 384, 640),
-                                   (1, 256, 21504)])
+                                   (1, 256, 21504), (5, 256, 130944),
+                                   (300, 384, 98304)])
 def test_linear(orc, M, N, K):
     say(f"linear M={M} N={N} K={K}")
     x = D.activations(M, K, seed=3)
@@ -374,7 +378,7 @@ RANDOM_SHAPES = [(3024, 3456, 640), (7666, 1152, 128), (1415, 1792, 512),
 @pytest.mark.parametrize("M,N,K", RANDOM_SHAPES)
 def test_gemm_random_shapes(orc, M, N, K):
     say(f"gemm random shape M={M} N={N} K={K} "
-        f"workspace={B.workspace_bytes(M, N, K)}")
+        f"workspace={B.gemm_workspace_bytes(M, N, K)}")
     a, w, sa, sw, bias = gemm_inputs(M, N, K, 12)
     args = (dev(a), dev(sa), dev(w), dev(sw), dev_bf16(bias))
     ig = Guarded((M, N), torch.int32)
@@ -407,7 +411,7 @@ def test_gemm_max_k_closed_form(M, N):
     am = vals[g.integers(0, len(vals), M)]
     wn = vals[g.integers(0, len(vals), N)]
     am[0], wn[0] = -128, -128   # the largest positive accumulator
-    say(f"gemm max K M={M} N={N} K={K} workspace={B.workspace_bytes(M, N, K)}")
+    say(f"gemm max K M={M} N={N} K={K} workspace={B.gemm_workspace_bytes(M, N, K)}")
     a = torch.from_numpy(am.astype(np.int8)).cuda()[:, None].expand(M, K) \
         .contiguous()
     w = torch.from_numpy(wn.astype(np.int8)).cuda()[:, None].expand(N, K) \
@@ -435,7 +439,7 @@ def test_gemm_tail_split(orc, M, N, K):
     # channel tile 128 channels; 32 tail tiles in 4 slices.  65541 x 128:
     # one channel tile, half of it past N, 257 tiles, the last (5 rows)
     # split in 2.
-    ws = B.workspace_bytes(M, N, K)
+    ws = B.gemm_workspace_bytes(M, N, K)
     say(f"gemm tail split M={M} N={N} K={K} workspace={ws}")
     assert ws > 0
     a, w, sa, sw, bias = gemm_inputs(M, N, K, 4)
@@ -474,7 +478,7 @@ def test_graph_replay(orc, M, N, K):
     hq = torch.empty((M, K), dtype=torch.int8, device="cuda")
     hs = torch.empty((M,), dtype=torch.float32, device="cuda")
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty((max(B.workspace_bytes(M, N, K), 256),),
+    ws = torch.empty((max(B.gemm_workspace_bytes(M, N, K), 256),),
                      dtype=torch.uint8, device="cuda")
 
     def enqueue():
@@ -520,7 +524,7 @@ def test_fused_qkv_equals_separate(orc, M):
     params = {p.name: D.proj_params(p, wl.seed, 0) for p in qkv}
     projs = {p.name: BL.upload_proj(p, params[p.name]) for p in qkv}
     fused = BL.fuse_qkv(dict(projs))["qkv"]
-    assert fused.N == 3 * H and B.workspace_bytes(M, 3 * H, H) >= 0
+    assert fused.N == 3 * H and B.gemm_workspace_bytes(M, 3 * H, H) >= 0
     x = D.activations(M, H, seed=11)
     q, s = B.quantize_act(dev_bf16(x))
     sep = [B.gemm(q, s, projs[n].w, projs[n].sw, projs[n].bias)
@@ -553,27 +557,9 @@ def test_gemm_deterministic():
 
 
 # ---------------------------------------------------------------------------
-# full-size DiT blocks, sampled rows
+# the single-projection workload (the full-size blocks and chains are in
+# test_gpu_fullsize.py)
 # ---------------------------------------------------------------------------
-
-def oracle_block_rows(orc, x_rows, params, mlp="silu", o_input="x"):
-    """Oracle of the block's data flow on a subset of token rows."""
-    out = {}
-    q, s = orc.quantize_act(x_rows)
-    out["xq"], out["xs"] = q, s
-    for n in ("q", "k", "v", "fc1"):
-        p = params[n]
-        out[n] = orc.linear(x_rows, p.w, p.sw, p.bias)
-    p = params["o"]
-    out["o"] = orc.linear(out["v"] if o_input == "v" else x_rows, p.w, p.sw,
-                          p.bias)
-    h = (orc.swiglu_bf16(out["fc1"]) if mlp == "swiglu"
-         else orc.silu_bf16(out["fc1"]))
-    out["hq"], out["hs"] = orc.quantize_act(h)
-    p = params["fc2"]
-    out["fc2"] = orc.linear(h, p.w, p.sw, p.bias)
-    return out
-
 
 def test_config0_single_projection(orc):
     wl = D.WORKLOADS[0]
@@ -585,84 +571,6 @@ def test_config0_single_projection(orc):
     y = B.gemm(q, s, dev(pp.w), dev(pp.sw), dev_bf16(pp.bias))
     torch.cuda.synchronize()
     assert np.array_equal(host_bf16(y), orc.linear(x, pp.w, pp.sw, pp.bias))
-
-
-# configs 1-3: the block at 4096, 19077 and 37503 tokens; 5: the pages' H3
-# operator shapes (Q/K/V 5376 -> 7168, O fed by V, SwiGLU over a fused
-# gate | up FC1 5376 -> 28672, FC2 14336 -> 5376) at 19077 tokens.
-# Where O reads X (configs 1-3) Q, K and V also run fused into one GEMM,
-# as the benchmark runs them.
-@pytest.mark.parametrize("config,fused", [(1, False), (2, False), (3, False),
-                                          (5, False), (1, True), (2, True),
-                                          (3, True)])
-def test_block_sampled_rows(orc, config, fused):
-    wl = D.WORKLOADS[config]
-    say(f"block config {config}: {wl.name} M={wl.M}, fused QKV {fused}")
-    params = D.block_params(wl, 0)
-    projs = {p.name: BL.upload_proj(p, params[p.name]) for p in wl.projs}
-    if fused:
-        projs = BL.fuse_qkv(projs)
-    x = D.activations(wl.M, D.HIDDEN, wl.seed)
-    runner = BL.BlockRunner(wl.M, fused_qkv=fused, projs=wl.projs,
-                            mlp=wl.mlp, o_input=wl.o_input)
-    out = runner.run(dev_bf16(x), projs)
-    torch.cuda.synchronize()
-    rows = D.row_sample(wl.M, 24, wl.seed)
-    ri = torch.from_numpy(rows).cuda()
-    ref = oracle_block_rows(orc, x[rows], params, wl.mlp, wl.o_input)
-    assert np.array_equal(runner.xq[0][ri].cpu().numpy(), ref["xq"])
-    assert np.array_equal(runner.xs[0][ri].cpu().numpy().view(np.uint32),
-                          ref["xs"].view(np.uint32))
-    for n in ("q", "k", "v", "o", "fc1"):
-        got = host_bf16(out[n][ri])
-        assert np.array_equal(got, ref[n]), n
-    assert np.array_equal(runner.hq[ri].cpu().numpy(), ref["hq"])
-    assert np.array_equal(runner.hs[ri].cpu().numpy().view(np.uint32),
-                          ref["hs"].view(np.uint32))
-    assert np.array_equal(host_bf16(out["fc2"][ri]), ref["fc2"])
-
-
-# configs 4 and 6 chain 50 blocks through the power-of-two renormalization;
-# the first two blocks of each chain (distinct weights per block) are
-# checked on sampled rows, including the renormalized block input.
-@pytest.mark.parametrize("config,fused", [(4, True), (6, False)])
-def test_chain_sampled_rows(orc, config, fused):
-    wl = D.WORKLOADS[config]
-    say(f"chain config {config}: {wl.name} M={wl.M}, first 2 blocks, "
-        f"fused QKV {fused}")
-    x = D.activations(wl.M, D.HIDDEN, wl.seed)
-    rows = D.row_sample(wl.M, 14, wl.seed)
-    ri = torch.from_numpy(rows).cuda()
-    runner = BL.BlockRunner(wl.M, fused_qkv=fused, projs=wl.projs,
-                            mlp=wl.mlp, o_input=wl.o_input)
-    xd = dev_bf16(x)
-    bufs = [torch.empty_like(xd), torch.empty_like(xd)]
-    xr = x[rows]
-    for b in range(2):
-        params = D.block_params(wl, b)
-        projs = {p.name: BL.upload_proj(p, params[p.name]) for p in wl.projs}
-        if fused:
-            projs = BL.fuse_qkv(projs)
-        # as the benchmark chains the sweep with fused QKV: the block input
-        # after the first comes quantized from pow2_renorm_quantize
-        out = runner.run(xd, projs, x_quantized=fused and b > 0)
-        ref = oracle_block_rows(orc, xr, params, wl.mlp, wl.o_input)
-        torch.cuda.synchronize()
-        assert np.array_equal(runner.xq[0][ri].cpu().numpy(), ref["xq"]), b
-        for n in ("q", "o", "fc1", "fc2"):
-            assert np.array_equal(host_bf16(out[n][ri]), ref[n]), (b, n)
-        if b == 0:
-            nxt = bufs[0]
-            if fused:
-                B.pow2_renorm_quantize(out["fc2"], out=(nxt, runner.xq[0],
-                                                        runner.xs[0]))
-            else:
-                B.pow2_renorm(out["fc2"], out=nxt)
-            torch.cuda.synchronize()
-            xr = orc.pow2_renorm(ref["fc2"])
-            assert np.array_equal(host_bf16(nxt[ri]), xr)
-            xd = nxt
-        del projs, params
 
 
 def test_gemm_epilogue_edge_values(orc):
@@ -723,3 +631,112 @@ def test_binding_rejects_mismatched_outputs():
         B.quantize_act(x, out=(torch.empty((8, 128), dtype=torch.int8,
                                            device="cuda"),
                                torch.empty(8, device="cuda")))
+
+
+# ---------------------------------------------------------------------------
+# boundary cases: tile addresses, argument alignment, side streams
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(4097, 4096, 1024), (64, 5376, 5376),
+                                   (1100, 2048, 896)])
+def test_gemm_tile_bases_across_bit31(orc, M, N, K):
+    """Operands placed in one device buffer so that A crosses an address
+    whose low 32 bits are 0x80000000 in the middle of its rows and W lies
+    just above it: many tiles' base addresses then have bit 31 of the low
+    word set (a buffer resource built from a sign-extended low word would
+    read from a wrong address).  Through the large-tile launch with its
+    split tail (4097), the split-K skinny launch (64) and the unsplit small
+    tiles (1100); accumulators and BF16 outputs against the oracle."""
+    say(f"gemm tile bases across bit 31 M={M} N={N} K={K}")
+    a, w, sa, sw, bias = gemm_inputs(M, N, K, 31)
+    buf = torch.empty(((1 << 32) + M * K + N * K + 4096,), dtype=torch.uint8,
+                      device="cuda")
+    base = buf.data_ptr()
+    # A's byte M*K/2 (rounded down to 256) lands on low word 0x80000000
+    oa = (0x80000000 - ((M * K // 2) & ~255) - base) % (1 << 32)
+    ow = oa + (M * K + 255) // 256 * 256
+    assert ow + N * K <= buf.numel() and (base + oa) % 256 == 0
+    lo = lambda o: (base + o) & 0xFFFFFFFF
+    assert lo(oa) < 0x80000000 <= lo(oa + M * K - 1) and lo(ow) >= 0x80000000
+    ad = buf[oa:oa + M * K].view(torch.int8).view(M, K)
+    wd = buf[ow:ow + N * K].view(torch.int8).view(N, K)
+    ad.copy_(torch.from_numpy(a))
+    wd.copy_(torch.from_numpy(w))
+    args = (ad, dev(sa), wd, dev(sw), dev_bf16(bias))
+    yi = B.gemm(*args, out_dtype=torch.int32)
+    yb = B.gemm(*args)
+    torch.cuda.synchronize()
+    want = orc.gemm_i32(a, w)
+    got = yi.cpu().numpy()
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} accumulators differ: {bad[:5].tolist()}"
+    _, rb = orc.epilogue(want, sa, sw, bias)
+    assert np.array_equal(host_bf16(yb), rb)
+    del ad, wd, buf
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 384, 640), (4097, 4096, 1024),
+                                   (64, 5376, 5376), (1100, 2048, 896)])
+def test_gemm_unaligned_scale_and_bias(orc, M, N, K):
+    """Channel scales only 4-byte aligned and biases only 2-byte aligned
+    (one element into larger arrays), through every launch path; BF16 and
+    FP32 outputs of w8a8_gemm and the BF16 output of w8a8_linear must equal
+    the oracle."""
+    say(f"gemm unaligned scale/bias M={M} N={N} K={K}")
+    a, w, sa, sw, bias = gemm_inputs(M, N, K, 33)
+    sw_big = torch.zeros(N + 4, dtype=torch.float32, device="cuda")
+    b_big = torch.zeros(N + 4, dtype=torch.bfloat16, device="cuda")
+    sw_d, b_d = sw_big[1:N + 1], b_big[1:N + 1]
+    sw_d.copy_(torch.from_numpy(sw))
+    b_d.copy_(dev_bf16(bias))
+    assert sw_d.data_ptr() % 16 == 4 and b_d.data_ptr() % 8 == 2
+    args = (dev(a), dev(sa), dev(w), sw_d, b_d)
+    yb = B.gemm(*args)
+    yf = B.gemm(*args, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rf, rb = orc.epilogue(orc.gemm_i32(a, w), sa, sw, bias)
+    assert np.array_equal(yf.cpu().numpy().view(np.uint32), rf.view(np.uint32))
+    assert np.array_equal(host_bf16(yb), rb)
+    x = D.activations(M, K, seed=34)
+    y = B.linear(dev_bf16(x), dev(w), sw_d, b_d)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16(y), orc.linear(x, w, sw, bias))
+
+
+def test_side_stream_without_workspace(orc):
+    """gemm() and linear() called with stream= another stream and no
+    workspace allocate their workspace (and output) on the current stream;
+    the binding marks them used by the other stream, so memory allocated and
+    overwritten on the current stream right after the call returns cannot
+    take them while the other stream's kernels still run."""
+    M, N, K = 4097, 4096, 1024       # split tail: a workspace is needed
+    say(f"side stream, internal workspace M={M} N={N} K={K}")
+    a, w, sa, sw, bias = gemm_inputs(M, N, K, 35)
+    x = D.activations(M, K, seed=35)
+    args = (dev(a), dev(sa), dev(w), dev(sw), dev_bf16(bias))
+    xd = dev_bf16(x)
+    # long work queued ahead on the side stream keeps the calls below pending
+    busy_w = torch.zeros((16128, 5376), dtype=torch.int8, device="cuda")
+    busy_q = torch.zeros((19077, 5376), dtype=torch.int8, device="cuda")
+    busy_s = torch.ones(19077, device="cuda")
+    busy_sw = torch.ones(16128, device="cuda")
+    busy_ws = torch.empty((max(B.gemm_workspace_bytes(19077, 16128, 5376),
+                               256),), dtype=torch.uint8, device="cuda")
+    busy_y = torch.empty((19077, 16128), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        B.gemm(busy_q, busy_s, busy_w, busy_sw, out=busy_y,
+               workspace=busy_ws, stream=side)
+    yg = B.gemm(*args, stream=side)
+    yl = B.linear(xd, args[2], args[3], args[4], stream=side)
+    need = max(B.workspace_bytes(M, N, K), M * N * 2)
+    junk = [torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
+            for _ in range(6)]
+    side.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    _, rb = orc.epilogue(orc.gemm_i32(a, w), sa, sw, bias)
+    assert np.array_equal(host_bf16(yg), rb)
+    assert np.array_equal(host_bf16(yl), orc.linear(x, w, sw, bias))

@@ -22,7 +22,7 @@ STATUS = {
     6: "W8A8_ERR_ALIAS", 7: "W8A8_ERR_DEVICE", 8: "W8A8_ERR_HIP",
 }
 MAX_K = 130944
-QUANT_MAX_K = 90112
+GLUE_MAX_K = 90112   # SiLU, renormalization and the fused quantizers
 
 # Every symbol include/w8a8.h declares, with its ctypes signature.
 _P, _I64, _SZ, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
@@ -34,9 +34,10 @@ SIGNATURES = {
     "w8a8_linear": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ,
                          _P]),
     "w8a8_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
-    "w8a8_linear_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "w8a8_gemm_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "w8a8_status_string": (ctypes.c_char_p, [_I]),
     "w8a8_last_hip_error": (_I, []),
+    "w8a8_build_id": (ctypes.c_char_p, []),
     "w8a8_silu_bf16": (_I, [_P, _P, _I64, _P]),
     "w8a8_pow2_renorm": (_I, [_P, _P, _I64, _I64, _P]),
     "w8a8_pow2_renorm_quantize": (_I, [_P, _I64, _I64, _P, _P, _P, _P]),
@@ -58,8 +59,34 @@ class W8A8Error(RuntimeError):
 _lib = None
 
 
+def _load(path):
+    L = ctypes.CDLL(str(path))
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
+def _expected_build_id() -> str:
+    from . import build as _build
+    return _build.source_sha256()
+
+
+def build_is_stale() -> bool:
+    """True when the shared object is missing or was compiled from sources
+    other than the ones beside it (read without keeping it loaded)."""
+    if not LIB_PATH.exists():
+        return True
+    if _lib is not None:
+        return _lib.w8a8_build_id().decode() != _expected_build_id()
+    return _load(LIB_PATH).w8a8_build_id().decode() != _expected_build_id()
+
+
 def lib():
-    """The loaded shared object (raises if it has not been built)."""
+    """The loaded shared object.  Raises if it has not been built, or if it
+    was built from other sources than the ones in the tree (a stale build
+    would run old kernels under new code)."""
     global _lib
     if _lib is None:
         if not LIB_PATH.exists():
@@ -67,11 +94,13 @@ def lib():
                 f"{LIB_PATH} is missing: build it with "
                 "`python -m w8a8_int8_gemm_amd.build` (or "
                 "__graft_entry__.build()); there is no fallback path")
-        L = ctypes.CDLL(str(LIB_PATH))
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(L, name)
-            fn.restype = res
-            fn.argtypes = args
+        L = _load(LIB_PATH)
+        got, want = L.w8a8_build_id().decode(), _expected_build_id()
+        if got != want:
+            raise ImportError(
+                f"{LIB_PATH} was built from other sources (build id "
+                f"{got[:12]}, sources {want[:12]}): rebuild it with "
+                "`python -m w8a8_int8_gemm_amd.build`")
         _lib = L
     return _lib
 
@@ -97,6 +126,21 @@ def _stream(stream=None):
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _on_stream(stream, *tensors):
+    """Tensors allocated here on torch's current stream but used by kernels
+    enqueued on another `stream`: tell the caching allocator, so that it does
+    not hand their memory to a later allocation on the current stream while
+    those kernels may still read or write it."""
+    if stream is None:
+        return
+    torch = _torch()
+    if stream == torch.cuda.current_stream():
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
 
 
 def _ptr(t):
@@ -139,15 +183,19 @@ def quantize_act(x, *, silu: bool = False, out=None, stream=None):
     fn = lib().w8a8_quantize_act_silu if silu else lib().w8a8_quantize_act
     _check("w8a8_quantize_act" + ("_silu" if silu else ""),
            fn(_ptr(x), M, K, _ptr(q), _ptr(s), _stream(stream)))
+    if out is None:
+        _on_stream(stream, q, s)
     return q, s
 
 
 def workspace_bytes(M: int, N: int, K: int) -> int:
+    """Bytes that serve both linear() and gemm() for this shape."""
     return int(lib().w8a8_workspace_bytes(M, N, K))
 
 
-def linear_workspace_bytes(M: int, N: int, K: int) -> int:
-    return int(lib().w8a8_linear_workspace_bytes(M, N, K))
+def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Bytes gemm() alone needs (its split-K partial sums)."""
+    return int(lib().w8a8_gemm_workspace_bytes(M, N, K))
 
 
 def _workspace(nbytes, device, given=None):
@@ -182,17 +230,20 @@ def gemm(a_q, a_scale, w_q, w_scale, bias=None, out_dtype=None, *, out=None,
     _need(w_scale, torch.float32, 1, "w_scale", (N,))
     if bias is not None:
         _need(bias, torch.bfloat16, 1, "bias", (N,))
-    if out is None:
+    own_out = out is None
+    if own_out:
         out = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
     else:
         _need(out, out_dtype, 2, "out", (M, N))
-    ws_need = workspace_bytes(M, N, K)
+    ws_need = gemm_workspace_bytes(M, N, K)
     ws = _workspace(ws_need, a_q.device, workspace)
     ws_len = 0 if ws is None else ws.numel() * ws.element_size()
     _check("w8a8_gemm", lib().w8a8_gemm(
         _ptr(a_q), _ptr(a_scale), _ptr(w_q), _ptr(w_scale), _ptr(bias),
         _ptr(out), codes[out_dtype], M, N, K, _ptr(ws), ws_len,
         _stream(stream)))
+    _on_stream(stream, out if own_out else None,
+               ws if workspace is None else None)
     return out
 
 
@@ -209,15 +260,18 @@ def linear(x, w_q, w_scale, bias=None, *, out=None, workspace=None,
     _need(w_scale, torch.float32, 1, "w_scale", (N,))
     if bias is not None:
         _need(bias, torch.bfloat16, 1, "bias", (N,))
-    if out is None:
+    own_out = out is None
+    if own_out:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     else:
         _need(out, torch.bfloat16, 2, "out", (M, N))
-    ws = _workspace(linear_workspace_bytes(M, N, K), x.device, workspace)
+    ws = _workspace(workspace_bytes(M, N, K), x.device, workspace)
     ws_len = 0 if ws is None else ws.numel() * ws.element_size()
     _check("w8a8_linear", lib().w8a8_linear(
         _ptr(x), _ptr(w_q), _ptr(w_scale), _ptr(bias), _ptr(out), M, N, K,
         _ptr(ws), ws_len, _stream(stream)))
+    _on_stream(stream, out if own_out else None,
+               ws if workspace is None else None)
     return out
 
 
@@ -228,6 +282,8 @@ def silu(x, *, out=None, stream=None):
     _need(y, torch.bfloat16, x.dim(), "out", tuple(x.shape))
     _check("w8a8_silu_bf16", lib().w8a8_silu_bf16(
         _ptr(x), _ptr(y), x.numel(), _stream(stream)))
+    if out is None:
+        _on_stream(stream, y)
     return y
 
 
@@ -239,6 +295,8 @@ def pow2_renorm(x, *, out=None, stream=None):
     _need(y, torch.bfloat16, 2, "out", (M, K))
     _check("w8a8_pow2_renorm", lib().w8a8_pow2_renorm(
         _ptr(x), _ptr(y), M, K, _stream(stream)))
+    if out is None:
+        _on_stream(stream, y)
     return y
 
 
@@ -260,6 +318,8 @@ def pow2_renorm_quantize(x, *, out=None, stream=None):
         _need(s, torch.float32, 1, "out[2]", (M,))
     _check("w8a8_pow2_renorm_quantize", lib().w8a8_pow2_renorm_quantize(
         _ptr(x), M, K, _ptr(y), _ptr(q), _ptr(s), _stream(stream)))
+    if out is None:
+        _on_stream(stream, y, q, s)
     return y, q, s
 
 
@@ -278,6 +338,8 @@ def quantize_weight(w, *, out=None, stream=None):
         _need(s, torch.float32, 1, "out[1]", (N,))
     _check("w8a8_quantize_weight", lib().w8a8_quantize_weight(
         _ptr(w), N, K, _ptr(q), _ptr(s), _stream(stream)))
+    if out is None:
+        _on_stream(stream, q, s)
     return q, s
 
 
@@ -290,6 +352,8 @@ def check_scales(w_scale, *, out=None, stream=None):
     _need(bad, torch.int32, 1, "out", (1,))
     _check("w8a8_check_scales", lib().w8a8_check_scales(
         _ptr(w_scale), w_scale.numel(), _ptr(bad), _stream(stream)))
+    if out is None:
+        _on_stream(stream, bad)
     return bad
 
 
@@ -305,6 +369,8 @@ def swiglu(h, *, out=None, stream=None):
     _need(y, torch.bfloat16, 2, "out", (M, F2 // 2))
     _check("w8a8_swiglu_bf16", lib().w8a8_swiglu_bf16(
         _ptr(h), _ptr(y), M, F2 // 2, _stream(stream)))
+    if out is None:
+        _on_stream(stream, y)
     return y
 
 
@@ -325,4 +391,6 @@ def quantize_act_swiglu(h, *, out=None, stream=None):
         _need(s, torch.float32, 1, "out[1]", (M,))
     _check("w8a8_quantize_act_swiglu", lib().w8a8_quantize_act_swiglu(
         _ptr(h), M, F2 // 2, _ptr(q), _ptr(s), _stream(stream)))
+    if out is None:
+        _on_stream(stream, q, s)
     return q, s

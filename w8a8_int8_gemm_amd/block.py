@@ -107,8 +107,8 @@ class BlockRunner:
         else:
             for n in ("q", "k", "v"):
                 self.out[n] = e(M, shape[n][0], dt=torch.bfloat16)
-        need = [B.workspace_bytes(M, N, K) for N, K in shape.values()]
-        need.append(B.workspace_bytes(M, 3 * shape["q"][0], H))
+        need = [B.gemm_workspace_bytes(M, N, K) for N, K in shape.values()]
+        need.append(B.gemm_workspace_bytes(M, 3 * shape["q"][0], H))
         self.ws = e(max(max(need), 256), dt=torch.uint8)
 
     def _gemm(self, projs, name, q, s, stream, on_gemm):

@@ -13,6 +13,7 @@ it.  hipcc cross-compiles without a GPU.  Flags:
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -23,6 +24,8 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libw8a8.so"
 SOURCES = ["w8a8_api.cpp", "rowwise.hip", "gemm.hip"]
+# Headers the library's sources include (part of its build id).
+HEADERS = [CSRC / "internal.h", CSRC / "rowwise.h", ROOT / "include" / "w8a8.h"]
 # Measurement support, not part of the library: the register-only MFMA
 # rate on given code matrices (loaded by bench.py only).
 CEILING_LIB = PKG / "libw8a8_ceiling.so"
@@ -38,12 +41,24 @@ FLAGS = [
 ]
 
 
+def source_sha256(sources: list[str] | None = None) -> str:
+    """SHA-256 over the named sources and the shared headers, in a fixed
+    order: the build id compiled into the library (w8a8_build_id), compared
+    by the binding against the files on disk to refuse a stale build."""
+    h = hashlib.sha256()
+    for f in [CSRC / s for s in (sources or SOURCES)] + HEADERS:
+        h.update(f.name.encode() + b"\0" + f.read_bytes())
+    return h.hexdigest()
+
+
 def build(extra: list[str] | None = None, out: Path = LIB,
           verbose: bool = False, sources: list[str] | None = None) -> Path:
     """Compile every HIP source of the library into one shared object."""
     tmp = out.with_name(out.name + ".tmp")
-    cmd = [HIPCC, *FLAGS, *(extra or []), "-o", str(tmp),
-           *[str(CSRC / s) for s in (sources or SOURCES)]]
+    srcs = sources or SOURCES
+    cmd = [HIPCC, *FLAGS, *(extra or []),
+           f'-DW8A8_SOURCE_SHA256="{source_sha256(srcs)}"', "-o", str(tmp),
+           *[str(CSRC / s) for s in srcs]]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -126,6 +126,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const int8_t *base) 
                                            (short)0, 0x7fffffff, 0x00020000);
 }
 
+// Four consecutive channel scales (biases) from channel n, a multiple of 4:
+// one vector load when the array is 16-byte (8-byte) aligned, else one
+// load per value (the boundary accepts 4-byte aligned scales and 2-byte
+// aligned biases, e.g. a channel slice of larger arrays).  `vec` is uniform
+// across the launch.
+__device__ __forceinline__ float4 load_scale4(const float *sw, int n,
+                                              bool vec) {
+  if (vec) return *reinterpret_cast<const float4 *>(sw + n);
+  return make_float4(sw[n], sw[n + 1], sw[n + 2], sw[n + 3]);
+}
+
+__device__ __forceinline__ float4 load_bias4(const uint16_t *b, int n,
+                                             bool vec) {
+  uint32_t b01, b23;
+  if (vec) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(b + n);
+    b01 = v.x;
+    b23 = v.y;
+  } else {
+    b01 = (uint32_t)b[n] | ((uint32_t)b[n + 1] << 16);
+    b23 = (uint32_t)b[n + 2] | ((uint32_t)b[n + 3] << 16);
+  }
+  return make_float4(bf16_to_f32(b01 & 0xFFFFu), bf16_to_f32(b01 >> 16),
+                     bf16_to_f32(b23 & 0xFFFFu), bf16_to_f32(b23 >> 16));
+}
+
 __device__ __forceinline__ v4i read_lds16(const int8_t *lds_base, int off) {
   return *reinterpret_cast<const v4i *>(lds_base + off);
 }
@@ -200,6 +226,8 @@ struct KernelArgs {
   int group_m;
   int tile_base;     // first tile index of this launch
   int remap;         // 1: XCD remap of block ids over the grid
+  int vec_sw;        // 1: sw is 16-byte aligned (vector loads)
+  int vec_bias;      // 1: bias is 8-byte aligned (vector loads)
 };
 
 template <class C, int EPI>
@@ -430,13 +458,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(KernelArgs p) {
         for (int g = 0; g < 4; ++g) {
           const int nl = i * 32 + 8 * g + 4 * (lane >> 5);
           const int n = nb + nl;
-          const float4 swn = *reinterpret_cast<const float4 *>(p.sw + n);
+          const float4 swn = load_scale4(p.sw, n, p.vec_sw);
           float4 bv;
-          if constexpr (kBias) {
-            const uint2 b = *reinterpret_cast<const uint2 *>(p.bias + n);
-            bv = make_float4(bf16_to_f32(b.x & 0xFFFFu), bf16_to_f32(b.x >> 16),
-                             bf16_to_f32(b.y & 0xFFFFu), bf16_to_f32(b.y >> 16));
-          }
+          if constexpr (kBias) bv = load_bias4(p.bias, n, p.vec_bias);
           const int c = nl >> 3, h = (nl >> 2) & 1;
 #pragma unroll
           for (int j = 0; j < C::TM; ++j) {
@@ -521,17 +545,17 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(KernelArgs p) {
           *reinterpret_cast<v4i *>(dst + o) = v4i{acc0, acc1, acc2, acc3};
           continue;
         }
-        const float4 swn = *reinterpret_cast<const float4 *>(p.sw + n);
+        const float4 swn = load_scale4(p.sw, n, p.vec_sw);
         float t0 = ((float)acc0 * sam) * swn.x;
         float t1 = ((float)acc1 * sam) * swn.y;
         float t2 = ((float)acc2 * sam) * swn.z;
         float t3 = ((float)acc3 * sam) * swn.w;
         if (p.bias) {
-          const uint2 b = *reinterpret_cast<const uint2 *>(p.bias + n);
-          t0 = t0 + bf16_to_f32(b.x & 0xFFFFu);
-          t1 = t1 + bf16_to_f32(b.x >> 16);
-          t2 = t2 + bf16_to_f32(b.y & 0xFFFFu);
-          t3 = t3 + bf16_to_f32(b.y >> 16);
+          const float4 bv = load_bias4(p.bias, n, p.vec_bias);
+          t0 = t0 + bv.x;
+          t1 = t1 + bv.y;
+          t2 = t2 + bv.z;
+          t3 = t3 + bv.w;
         }
         if (EPI == EPI_FP32) {
           *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + o) =
@@ -552,7 +576,7 @@ template <int EPI>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(
     const int *__restrict__ part, int splits, const float *__restrict__ sa,
     const float *__restrict__ sw, const uint16_t *__restrict__ bias,
-    void *__restrict__ out, int M, int N) {
+    void *__restrict__ out, int M, int N, bool vec_sw, bool vec_bias) {
   const int64_t MN = (int64_t)M * N;
   const int64_t quads = MN / 4;
   for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < quads;
@@ -578,17 +602,17 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
     const int m = (int)(o / N);
     const int n = (int)(o - (int64_t)m * N);
     const float sam = sa[m];
-    const float4 swn = *reinterpret_cast<const float4 *>(sw + n);
+    const float4 swn = load_scale4(sw, n, vec_sw);
     float t0 = ((float)s.x * sam) * swn.x;
     float t1 = ((float)s.y * sam) * swn.y;
     float t2 = ((float)s.z * sam) * swn.z;
     float t3 = ((float)s.w * sam) * swn.w;
     if (bias) {
-      const uint2 b = *reinterpret_cast<const uint2 *>(bias + n);
-      t0 = t0 + bf16_to_f32(b.x & 0xFFFFu);
-      t1 = t1 + bf16_to_f32(b.x >> 16);
-      t2 = t2 + bf16_to_f32(b.y & 0xFFFFu);
-      t3 = t3 + bf16_to_f32(b.y >> 16);
+      const float4 bv = load_bias4(bias, n, vec_bias);
+      t0 = t0 + bv.x;
+      t1 = t1 + bv.y;
+      t2 = t2 + bv.z;
+      t3 = t3 + bv.w;
     }
     if (EPI == EPI_FP32) {
       *reinterpret_cast<float4 *>(static_cast<float *>(out) + o) =
@@ -611,7 +635,7 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(
     const int *__restrict__ part, int splits, int ntail, int tile_base,
     int tiles_m, int tiles_n, int group_m, const float *__restrict__ sa,
     const float *__restrict__ sw, const uint16_t *__restrict__ bias,
-    void *__restrict__ out, int M, int N) {
+    void *__restrict__ out, int M, int N, bool vec_sw, bool vec_bias) {
   constexpr int QB = C::BM * C::BN / 4 / 256;
   const int t = blockIdx.x / QB;
   const int q = (blockIdx.x % QB) * 256 + threadIdx.x;
@@ -644,17 +668,17 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(
     return;
   }
   const float sam = sa[m];
-  const float4 swn = *reinterpret_cast<const float4 *>(sw + n);
+  const float4 swn = load_scale4(sw, n, vec_sw);
   float t0 = ((float)s.x * sam) * swn.x;
   float t1 = ((float)s.y * sam) * swn.y;
   float t2 = ((float)s.z * sam) * swn.z;
   float t3 = ((float)s.w * sam) * swn.w;
   if (bias) {
-    const uint2 b = *reinterpret_cast<const uint2 *>(bias + n);
-    t0 = t0 + bf16_to_f32(b.x & 0xFFFFu);
-    t1 = t1 + bf16_to_f32(b.x >> 16);
-    t2 = t2 + bf16_to_f32(b.y & 0xFFFFu);
-    t3 = t3 + bf16_to_f32(b.y >> 16);
+    const float4 bv = load_bias4(bias, n, vec_bias);
+    t0 = t0 + bv.x;
+    t1 = t1 + bv.y;
+    t2 = t2 + bv.z;
+    t3 = t3 + bv.w;
   }
   if (EPI == EPI_FP32) {
     *reinterpret_cast<float4 *>(static_cast<float *>(out) + o) =
@@ -737,6 +761,10 @@ hipError_t launch_cfg(const GemmArgs &g, const GemmPlan &plan,
   p.group_m = plan.group_m;
   p.tile_base = 0;
   p.remap = 1;
+  const bool vb_sw = (reinterpret_cast<uintptr_t>(g.sw) & 15) == 0;
+  const bool vb_bias = (reinterpret_cast<uintptr_t>(g.bias) & 7) == 0;
+  p.vec_sw = vb_sw;
+  p.vec_bias = vb_bias;
   const dim3 grid((unsigned)plan.main_tiles, 1, (unsigned)plan.splits);
   if (plan.splits == 1) {
     p.out = g.out;
@@ -766,7 +794,7 @@ hipError_t launch_cfg(const GemmArgs &g, const GemmPlan &plan,
   hipLaunchKernelGGL((tail_reduce_kernel<C, E>), rgrid, dim3(256),           \
                      0, stream, part, plan.tail_splits, plan.tail_tiles,     \
                      plan.main_tiles, p.tiles_m, p.tiles_n, p.group_m, g.sa, \
-                     g.sw, g.bias, g.out, p.M, p.N)
+                     g.sw, g.bias, g.out, p.M, p.N, vb_sw, vb_bias)
     switch (g.epi) {
       case EPI_BF16: W8A8_TAIL(EPI_BF16); break;
       case EPI_FP32: W8A8_TAIL(EPI_FP32); break;
@@ -787,17 +815,17 @@ hipError_t launch_cfg(const GemmArgs &g, const GemmPlan &plan,
     case EPI_BF16:
       hipLaunchKernelGGL(splitk_reduce_kernel<EPI_BF16>, dim3((unsigned)blocks),
                          dim3(256), 0, stream, part, plan.splits, g.sa, g.sw,
-                         g.bias, g.out, p.M, p.N);
+                         g.bias, g.out, p.M, p.N, vb_sw, vb_bias);
       break;
     case EPI_FP32:
       hipLaunchKernelGGL(splitk_reduce_kernel<EPI_FP32>, dim3((unsigned)blocks),
                          dim3(256), 0, stream, part, plan.splits, g.sa, g.sw,
-                         g.bias, g.out, p.M, p.N);
+                         g.bias, g.out, p.M, p.N, vb_sw, vb_bias);
       break;
     default:
       hipLaunchKernelGGL(splitk_reduce_kernel<EPI_I32>, dim3((unsigned)blocks),
                          dim3(256), 0, stream, part, plan.splits, g.sa, g.sw,
-                         g.bias, g.out, p.M, p.N);
+                         g.bias, g.out, p.M, p.N, vb_sw, vb_bias);
       break;
   }
   return hipGetLastError();

@@ -250,6 +250,43 @@ __global__ __launch_bounds__(kThreads) void row_kernel(
   }
 }
 
+// Quantization of rows longer than the register-resident kernel holds
+// (K > 90112, up to the GEMM's INT32 bound): one work group per row reads
+// the row twice, first for its maximum and then for the codes, with the
+// same arithmetic as row_kernel.
+template <int OP>
+__global__ __launch_bounds__(kThreads) void long_row_quant_kernel(
+    const uint16_t *x, int8_t *q, float *__restrict__ scale, int K) {
+  __shared__ float part_max[kWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = blockIdx.x;
+  const int chunks = K >> 3;
+  const v4u *xr = reinterpret_cast<const v4u *>(x + row * (int64_t)K);
+  us2 mag = us2{0, 0};
+  for (int j = threadIdx.x; j < chunks; j += kThreads)
+    mag = mag_max4(mag, xr[j]);
+  float amax = wave_max(mag_to_f32(mag));
+  if (lane == 0) part_max[wave] = amax;
+  __syncthreads();
+  amax = part_max[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) amax = fmaxf(amax, part_max[w]);
+  const QuantRow R = quant_row(amax);
+  if (threadIdx.x == 0)
+    scale[row] = (OP == OP_QUANT_W && R.s == 0.0f) ? 1.0f : R.s;
+  uint2 *qr = reinterpret_cast<uint2 *>(q + row * (int64_t)K);
+  for (int j = threadIdx.x; j < chunks; j += kThreads) {
+    uint2 o = make_uint2(0, 0);
+    if (R.s != 0.0f) {
+      const v4u c = xr[j];  // the second read of the row, likely cached
+      o.x = quant4(c.x, c.y, R);
+      o.y = quant4(c.z, c.w, R);
+    }
+    qr[j] = o;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // SiLU through a lookup table
 // ---------------------------------------------------------------------------
@@ -556,6 +593,14 @@ hipError_t launch_row_op(const uint16_t *x, void *out, float *scale,
                          int64_t M, int64_t K, hipStream_t stream,
                          uint16_t *aux = nullptr) {
   const int chunks = (int)(K / 8);
+  if constexpr (OP == OP_QUANT || OP == OP_QUANT_W) {
+    if (chunks > 44 * 4 * 64) {
+      hipLaunchKernelGGL((long_row_quant_kernel<OP>), dim3((unsigned)M),
+                         dim3(kThreads), 0, stream, x,
+                         static_cast<int8_t *>(out), scale, (int)K);
+      return hipGetLastError();
+    }
+  }
   if (chunks <= 11 * 64) {
     const int ch = (chunks + 63) / 64;
     return launch_rows<1, OP>(x, out, scale, M, (int)K, ch, stream, aux);

@@ -19,9 +19,13 @@ namespace {
 using w8a8::GemmArgs;
 using w8a8::GemmPlan;
 
-// Largest K the quantizer's register-resident rows cover (44 chunks of 8
-// BF16 per lane x 4 waves x 64 lanes).
-constexpr int64_t kQuantMaxK = 44 * 8 * 4 * 64;
+// Largest K the register-resident row kernels cover (44 chunks of 8 BF16
+// per lane x 4 waves x 64 lanes): the glue kernels (SiLU, renormalization)
+// and the fused quantizers.  The plain quantizers (activations, weights)
+// take longer rows, up to W8A8_MAX_K, through a kernel that reads each row
+// twice.
+constexpr int64_t kGlueMaxK = 44 * 8 * 4 * 64;
+constexpr int64_t kQuantMaxK = W8A8_MAX_K;
 constexpr int64_t kMaxRows = 0x7FFFFFFF;
 // Rows of the per-token kernels: their launches hold up to 256 work-items
 // per row, and a launch holds fewer than 2^32 work-items.
@@ -78,9 +82,9 @@ bool gemm_shape_ok(int64_t M, int64_t N, int64_t K) {
 }
 
 int validate_quant(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
-                   const float *sa) {
+                   const float *sa, int64_t max_k = kQuantMaxK) {
   if (!x || !q || !sa) return W8A8_ERR_NULL;
-  if (M < 1 || M > kMaxTokenRows || K < 8 || K % 8 != 0 || K > kQuantMaxK)
+  if (M < 1 || M > kMaxTokenRows || K < 8 || K % 8 != 0 || K > max_k)
     return W8A8_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(q, 8) || !aligned(sa, 4))
     return W8A8_ERR_ALIGN;
@@ -110,15 +114,15 @@ int validate_gemm(const int8_t *a_q, const float *a_scale, const int8_t *w_q,
   const int eb = out_elem_bytes(out_dtype);
   if (eb == 0) return W8A8_ERR_OUT_DTYPE;
   if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(out, 16) ||
-      !aligned(w_scale, 16) || !aligned(a_scale, 4) ||
-      (bias && !aligned(bias, 8)))
+      !aligned(w_scale, 4) || !aligned(a_scale, 4) ||
+      (bias && !aligned(bias, 2)))
     return W8A8_ERR_ALIGN;
   *plan = w8a8::plan_gemm(M, N, K);
   if (!w8a8::plan_launchable(*plan)) return W8A8_ERR_SHAPE;
   if (plan->workspace > 0) {
     if (!workspace || workspace_bytes < plan->workspace)
       return W8A8_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return W8A8_ERR_ALIGN;
+    if (!aligned(workspace, 16)) return W8A8_ERR_ALIGN;
   }
   const Range ro = range_of(out, M * N * eb);
   const Range ins[] = {range_of(a_q, M * K), range_of(a_scale, M * 4),
@@ -156,13 +160,18 @@ const char *w8a8_status_string(int status) {
 
 int w8a8_last_hip_error(void) { return g_last_hip_error; }
 
-size_t w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+#ifndef W8A8_SOURCE_SHA256
+#define W8A8_SOURCE_SHA256 "unknown"
+#endif
+const char *w8a8_build_id(void) { return W8A8_SOURCE_SHA256; }
+
+size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (!gemm_shape_ok(M, N, K)) return 0;
   return w8a8::plan_gemm(M, N, K).workspace;
 }
 
-size_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (!gemm_shape_ok(M, N, K)) return 0;
+size_t w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (!gemm_shape_ok(M, N, K) || M > kMaxTokenRows) return 0;
   return round_up((size_t)(M * K), 256) + round_up((size_t)M * 4, 256) +
          w8a8::plan_gemm(M, N, K).workspace;
 }
@@ -178,7 +187,7 @@ int w8a8_quantize_act(const uint16_t *x, int64_t M, int64_t K, int8_t *a_q,
 
 int w8a8_quantize_act_silu(const uint16_t *x, int64_t M, int64_t K,
                            int8_t *a_q, float *a_scale, void *stream) {
-  int st = validate_quant(x, M, K, a_q, a_scale);
+  int st = validate_quant(x, M, K, a_q, a_scale, kGlueMaxK);
   if (st != W8A8_OK) return st;
   if ((st = check_device()) != W8A8_OK) return st;
   return hip_status(w8a8::launch_quantize_act(
@@ -208,9 +217,9 @@ int w8a8_linear(const uint16_t *x, const int8_t *w_q, const float *w_scale,
   if (!gemm_shape_ok(M, N, K) || K > kQuantMaxK || M > kMaxTokenRows)
     return W8A8_ERR_SHAPE;
   if (!aligned(x, 16)) return W8A8_ERR_ALIGN;
-  const size_t need = w8a8_linear_workspace_bytes(M, N, K);
+  const size_t need = w8a8_workspace_bytes(M, N, K);
   if (!workspace || workspace_bytes < need) return W8A8_ERR_WORKSPACE;
-  if (!aligned(workspace, 256)) return W8A8_ERR_ALIGN;
+  if (!aligned(workspace, 16)) return W8A8_ERR_ALIGN;
   int8_t *aq = static_cast<int8_t *>(workspace);
   float *sa = reinterpret_cast<float *>(static_cast<char *>(workspace) +
                                         round_up((size_t)(M * K), 256));
@@ -278,7 +287,7 @@ int w8a8_swiglu_bf16(const uint16_t *h, uint16_t *y, int64_t M, int64_t F,
 int w8a8_quantize_act_swiglu(const uint16_t *h, int64_t M, int64_t F,
                              int8_t *a_q, float *a_scale, void *stream) {
   if (!h || !a_q || !a_scale) return W8A8_ERR_NULL;
-  if (M < 1 || M > kMaxTokenRows || F < 8 || F % 8 != 0 || F > kQuantMaxK)
+  if (M < 1 || M > kMaxTokenRows || F < 8 || F % 8 != 0 || F > kGlueMaxK)
     return W8A8_ERR_SHAPE;
   if (!aligned(h, 16) || !aligned(a_q, 8) || !aligned(a_scale, 4))
     return W8A8_ERR_ALIGN;
@@ -307,7 +316,7 @@ int w8a8_silu_bf16(const uint16_t *x, uint16_t *y, int64_t n, void *stream) {
 int w8a8_pow2_renorm(const uint16_t *x, uint16_t *y, int64_t M, int64_t K,
                      void *stream) {
   if (!x || !y) return W8A8_ERR_NULL;
-  if (M < 1 || M > kMaxTokenRows || K < 8 || K % 8 != 0 || K > kQuantMaxK)
+  if (M < 1 || M > kMaxTokenRows || K < 8 || K % 8 != 0 || K > kGlueMaxK)
     return W8A8_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(y, 16)) return W8A8_ERR_ALIGN;
   if (x != y && overlap(range_of(x, M * K * 2), range_of(y, M * K * 2)))
@@ -322,7 +331,7 @@ int w8a8_pow2_renorm_quantize(const uint16_t *x, int64_t M, int64_t K,
                               uint16_t *y, int8_t *a_q, float *a_scale,
                               void *stream) {
   if (!x || !y || !a_q || !a_scale) return W8A8_ERR_NULL;
-  if (M < 1 || M > kMaxTokenRows || K < 8 || K % 8 != 0 || K > kQuantMaxK)
+  if (M < 1 || M > kMaxTokenRows || K < 8 || K % 8 != 0 || K > kGlueMaxK)
     return W8A8_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(a_q, 8) ||
       !aligned(a_scale, 4))
