@@ -79,3 +79,57 @@ def test_gemm_mix_fuses_qkv_into_one_call():
     assert tokens == 19077 and len(sep) == 6 and len(fused) == 4
     assert (3 * 5376, 5376) in fused and sep.count((5376, 5376)) == 4
     assert sum(n for n, _ in sep) == sum(n for n, _ in fused)
+
+
+def test_defaults_check_sixteen_rows_and_other_configs():
+    a = bench.parse([])
+    assert a.check_rows >= 16 and a.config == 4 and not a.no_per_config
+    assert set(bench.PER_CONFIGS) == {0, 1, 2, 3}
+
+
+def test_quant_bytes():
+    M, K = 19077, 5376
+    assert bench.quant_bytes("quant", M, K) == 2 * M * K + M * K + 4 * M
+    assert bench.quant_bytes("silu_quant", M, 21504) == 3 * M * 21504 + 4 * M
+    # gated: reads gate and up (2K wide), writes K codes
+    assert bench.quant_bytes("swiglu_quant", M, K) == 4 * M * K + M * K + 4 * M
+    # renormalization writes the BF16 row as well as the codes
+    assert bench.quant_bytes("renorm_quant", M, K) == 5 * M * K + 4 * M
+
+
+def test_step_stats_and_phases():
+    st = bench.step_stats([2.0, 4.0, 3.0])
+    assert st["median"] == 3.0 and st["n"] == 3 and st["std"] == 1.0
+    M = 100
+    stats = {"gemm:q": [2, 0.02, [(M, 256, 512)] * 2],
+             "quant": [4, 0.008, [(M, 512)] * 4]}
+    ph = bench.phases_entry(stats, M)
+    assert ph["gemm:q"]["avg_us"] == 10.0
+    assert ph["gemm:q"]["tops"] == round(2 * M * 256 * 512 / 1e-5 / 1e12, 2)
+    assert ph["quant"]["avg_us"] == 2.0
+    assert ph["quant"]["gbs"] == round(bench.quant_bytes("quant", M, 512)
+                                       / 2e-6 / 1e9, 1)
+    n, ms, ops = bench.gemm_totals(stats)
+    assert n == 2 and ms == 0.02 and ops == 2 * 2 * M * 256 * 512
+
+
+def test_power_clock_sampler_parses_amd_smi_json(tmp_path):
+    s = bench.PowerClockSampler.__new__(bench.PowerClockSampler)
+    s.proc = None
+    s.path = str(tmp_path / "smi.txt")
+    reading = {"gpu_data": [{"gpu": 0,
+                             "power": {"socket_power": {"value": 1400,
+                                                        "unit": "W"}},
+                             "clock": {f"gfx_{i}": {"clk": {"value": 1700 + i,
+                                                            "unit": "MHz"}}
+                                       for i in range(8)}}]}
+    with open(s.path, "w") as f:
+        for t in (10.0, 11.0, 12.0):
+            f.write(f"T {t}\n{json.dumps(reading)}\n")
+        f.write("T 13.0\nnot json\n")
+    assert len(s.samples()) == 3
+    w = s.window(10.5, 12.5)
+    assert w["samples"] == 2 and w["socket_power_w"] == [1400, 1400]
+    assert w["gfx_clock_mhz_min_mean_max"] == [1700, 1704, 1707]
+    assert w["xcds"] == 8
+    assert s.window(20, 30) is None

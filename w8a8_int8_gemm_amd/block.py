@@ -79,7 +79,8 @@ class BlockRunner:
     "swiglu" for a fused gate | up FC1; ``o_input``: "x", or "v" to feed
     V's output to the attention output projection).  ``run`` enqueues the
     block's kernels on the current stream (or ``stream``).  ``on_gemm`` is
-    called around every GEMM launch (for per-kernel event timing)."""
+    called around every GEMM launch and ``on_quant`` around every
+    quantization (for per-kernel event timing), as ``f(name, phase)``."""
 
     def __init__(self, M: int, device="cuda", fused_qkv: bool = False,
                  projs=D.BLOCK_PROJS, mlp: str = "silu", o_input: str = "x"):
@@ -141,7 +142,7 @@ class BlockRunner:
         return {n: src[n] for n in projs}
 
     def run(self, x, projs: dict, stream=None, on_gemm=None,
-            x_quantized: bool = False):
+            x_quantized: bool = False, on_quant=None):
         """x: bf16 [M, H].  Returns the dict of BF16 outputs.  With
         ``x_quantized`` the buffers ``xq[0]``, ``xs[0]`` already hold the
         quantization of x (written together with x by
@@ -149,29 +150,36 @@ class BlockRunner:
         def gemm(name, q, s):
             self._gemm(projs, name, q, s, stream, on_gemm)
 
+        def quant(name, fn, *a, **kw):
+            if on_quant:
+                on_quant(name, "begin")
+            fn(*a, stream=stream, **kw)
+            if on_quant:
+                on_quant(name, "end")
+
         # Q, K, V: one shared quantization of the block input (and, fused,
         # one GEMM over the concatenated weights).
         if not x_quantized:
-            B.quantize_act(x, out=(self.xq[0], self.xs[0]), stream=stream)
+            quant("quant", B.quantize_act, x, out=(self.xq[0], self.xs[0]))
         for n in (("qkv",) if "qkv" in projs else ("q", "k", "v")):
             gemm(n, self.xq[0], self.xs[0])
         # attention output projection and FC1 quantize their own inputs.
         if self.o_input == "v":
-            B.quantize_act(self.out["v"], out=(self.oq, self.xs[1]),
-                           stream=stream)
+            quant("quant_o", B.quantize_act, self.out["v"],
+                  out=(self.oq, self.xs[1]))
             gemm("o", self.oq, self.xs[1])
         else:
-            B.quantize_act(x, out=(self.xq[1], self.xs[1]), stream=stream)
+            quant("quant", B.quantize_act, x, out=(self.xq[1], self.xs[1]))
             gemm("o", self.xq[1], self.xs[1])
-        B.quantize_act(x, out=(self.xq[2], self.xs[2]), stream=stream)
+        quant("quant", B.quantize_act, x, out=(self.xq[2], self.xs[2]))
         gemm("fc1", self.xq[2], self.xs[2])
         # FC2 input: SiLU (or SwiGLU of gate | up) of FC1's BF16 output,
         # quantized in the same pass.
         if self.mlp == "swiglu":
-            B.quantize_act_swiglu(self.out["fc1"], out=(self.hq, self.hs),
-                                  stream=stream)
+            quant("swiglu_quant", B.quantize_act_swiglu, self.out["fc1"],
+                  out=(self.hq, self.hs))
         else:
-            B.quantize_act(self.out["fc1"], silu=True,
-                           out=(self.hq, self.hs), stream=stream)
+            quant("silu_quant", B.quantize_act, self.out["fc1"], silu=True,
+                  out=(self.hq, self.hs))
         gemm("fc2", self.hq, self.hs)
         return self.out
