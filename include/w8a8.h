@@ -122,6 +122,26 @@ int w8a8_gemm(const int8_t *a_q, const float *a_scale, const int8_t *w_q,
               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * w8a8_gemm without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Arguments, results and errors as w8a8_gemm;
+ * the split-K partial sums go to a device array the library holds, one
+ * copy of W8A8_NOALLOC_SCRATCH_BYTES per GPU for the life of the process
+ * (no call allocates or frees anything).  Every shape w8a8_gemm accepts
+ * fits: its partial sums never exceed that size (W8A8_ERR_WORKSPACE
+ * otherwise).  Calls of this entry point that overlap in time on one GPU
+ * (on different streams, or from different threads) share that array and
+ * race: order them on one stream.  The array's contents between calls do
+ * not matter (nothing in it needs clearing).  The array's address is
+ * looked up once per GPU at the first call of any entry point there.
+ */
+#define W8A8_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int w8a8_gemm_noalloc(const int8_t *a_q, const float *a_scale,
+                      const int8_t *w_q, const float *w_scale,
+                      const uint16_t *bias, void *out, int out_dtype,
+                      int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
  * Whole projection, the quantized Linear that replaces a BF16 Linear on
  * each of the six block projections ("feat(mps): support MiniMax-H3 INT8
  * inference on Apple M5", LightX2V pull request #1672, description: W8A8

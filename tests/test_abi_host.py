@@ -318,3 +318,35 @@ def test_mfma_ceiling_library_host_side():
         assert lib.w8a8_ceiling_run(a["x"], a["xr"], a["w"], a["wr"], a["K"],
                                     a["blocks"], a["iters"], a["out"],
                                     None) == 1, bad
+
+
+def test_noalloc_entry_validates_and_fits_every_plan():
+    """w8a8_gemm_noalloc checks its arguments like w8a8_gemm (no workspace
+    arguments), and the planner's partial sums fit its scratch for every
+    shape: tails of fewer than 256 tiles, skinny split-K grids."""
+    lib = B.lib()
+    f = lib.w8a8_gemm_noalloc
+    ok = dict(aq=BUF["aq"], sa=BUF["sa"], w=BUF["w"], sw=BUF["sw"],
+              bias=BUF["bias"], out=BUF["out"], dt=0, M=64, N=5376, K=5376)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["aq"], a["sa"], a["w"], a["sw"], a["bias"], a["out"],
+                 a["dt"], a["M"], a["N"], a["K"], None)
+    assert call(aq=None) == NULL
+    assert call(N=100) == SHAPE
+    assert call(dt=7) == OUT_DTYPE
+    assert call(sw=BUF["sw"] + 2) == ALIGN
+    assert call(out=BUF["w"]) == ALIAS
+    import torch
+    if torch.cuda.device_count() == 0:
+        assert call() == DEVICE
+    cap = B.NOALLOC_SCRATCH_BYTES
+    import itertools
+    worst = 0
+    for M, N, K in itertools.product(
+            [1, 17, 64, 255, 256, 300, 1100, 4096, 4097, 19077, 37503, 65541],
+            [128, 384, 2048, 4096, 5376, 16128, 21504, 28672],
+            [128, 640, 5376, 21504, B.MAX_K]):
+        worst = max(worst, B.gemm_workspace_bytes(M, N, K))
+    assert 0 < worst <= cap

@@ -33,6 +33,8 @@ SIGNATURES = {
                        _SZ, _P]),
     "w8a8_linear": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ,
                          _P]),
+    "w8a8_gemm_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _I, _I64, _I64,
+                               _I64, _P]),
     "w8a8_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "w8a8_gemm_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "w8a8_status_string": (ctypes.c_char_p, [_I]),
@@ -244,6 +246,38 @@ def gemm(a_q, a_scale, w_q, w_scale, bias=None, out_dtype=None, *, out=None,
         _stream(stream)))
     _on_stream(stream, out if own_out else None,
                ws if workspace is None else None)
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def gemm_noalloc(a_q, a_scale, w_q, w_scale, bias=None, out_dtype=None, *,
+                 out, stream=None):
+    """gemm() without a workspace: the split-K partial sums go to the
+    library's own device scratch (w8a8_gemm_noalloc).  ``out`` must be
+    given (nothing is allocated).  Calls that overlap in time on one GPU
+    share that scratch: keep them on one stream."""
+    torch = _torch()
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    codes = {torch.bfloat16: OUT_BF16, torch.float32: OUT_FP32,
+             torch.int32: OUT_I32}
+    if out_dtype not in codes:
+        raise ValueError(f"out_dtype {out_dtype} not supported")
+    _need(a_q, torch.int8, 2, "a_q")
+    M, K = a_q.shape
+    _need(w_q, torch.int8, 2, "w_q")
+    N = w_q.shape[0]
+    if w_q.shape[1] != K:
+        raise ValueError("a_q and w_q disagree on K")
+    _need(a_scale, torch.float32, 1, "a_scale", (M,))
+    _need(w_scale, torch.float32, 1, "w_scale", (N,))
+    if bias is not None:
+        _need(bias, torch.bfloat16, 1, "bias", (N,))
+    _need(out, out_dtype, 2, "out", (M, N))
+    _check("w8a8_gemm_noalloc", lib().w8a8_gemm_noalloc(
+        _ptr(a_q), _ptr(a_scale), _ptr(w_q), _ptr(w_scale), _ptr(bias),
+        _ptr(out), codes[out_dtype], M, N, K, _stream(stream)))
     return out
 
 

@@ -893,6 +893,43 @@ constexpr int kCUs = 256;
 
 }  // namespace
 
+// Scratch of w8a8_gemm_noalloc (callers that cannot allocate device
+// memory): the INT32 partial sums of the split-K launches live here instead
+// of in a caller's workspace.  The planner never needs more than 64 MiB of
+// partials: a split tail has fewer than 256 tiles, and tiles x slices stays
+// at or below 256 slices of one 256 x 256 INT32 tile (256 KiB each); the
+// skinny split-K plans at most 256 / tiles slices of an M x N tile grid of
+// 64 x 128 tiles, at most 8 MiB.  Host code never passes the array's name
+// to a kernel (in host code it is a stand-in, not a device address): it
+// uses the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+std::unordered_map<int, void *> g_scratch_addr;
+}  // namespace
+
+hipError_t resolve_scratch(int device) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr.count(device)) return hipSuccess;
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  if (cur != device) return hipErrorInvalidDevice;
+  void *ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (ptr == nullptr) return hipErrorInvalidSymbol;
+  g_scratch_addr[device] = ptr;
+  return hipSuccess;
+}
+
+void *scratch_on_device(int device) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  const auto it = g_scratch_addr.find(device);
+  return it == g_scratch_addr.end() ? nullptr : it->second;
+}
+
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   GemmPlan plan{kCfgLarge, 1, CfgLarge::GROUP_M, 0, 0, 0, 0};
   const int64_t tiles_n = (N + CfgLarge::BN - 1) / CfgLarge::BN;

@@ -132,6 +132,14 @@ struct GemmPlan {
 };
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
+
+// Device scratch of the allocation-free GEMM entry point: a file-scope
+// device array in gemm.hip, one copy per GPU.  resolve_scratch() looks up
+// this device's copy once (with the device current) and caches it;
+// scratch_on_device() then returns it (nullptr if never resolved).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+hipError_t resolve_scratch(int device);
+void *scratch_on_device(int device);
 // Whether every launch of the plan fits the hardware grid limits.
 bool plan_launchable(const GemmPlan &plan);
 hipError_t launch_gemm(const GemmArgs &args, const GemmPlan &plan,

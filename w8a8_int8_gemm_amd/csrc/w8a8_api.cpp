@@ -66,6 +66,10 @@ int check_device() {
   if (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
       std::strncmp(prop.gcnArchName, "gfx950", 6) == 0)
     status = W8A8_OK;
+  // Set-up on the first call on a gfx950 device, with it current: the
+  // address of this device's copy of the allocation-free entry point's
+  // scratch (a failure is reported by that entry point, which retries).
+  if (status == W8A8_OK) (void)w8a8::resolve_scratch(dev);
   checked[dev] = status;
   return status;
 }
@@ -104,11 +108,13 @@ int out_elem_bytes(int out_dtype) {
   }
 }
 
-int validate_gemm(const int8_t *a_q, const float *a_scale, const int8_t *w_q,
-                  const float *w_scale, const uint16_t *bias, const void *out,
-                  int out_dtype, int64_t M, int64_t N, int64_t K,
-                  const void *workspace, size_t workspace_bytes,
-                  GemmPlan *plan) {
+// Everything w8a8_gemm checks except its workspace: pointers, shape,
+// output type, alignment, a launchable plan and overlaps between the
+// output and the inputs.
+int validate_gemm_args(const int8_t *a_q, const float *a_scale,
+                       const int8_t *w_q, const float *w_scale,
+                       const uint16_t *bias, const void *out, int out_dtype,
+                       int64_t M, int64_t N, int64_t K, GemmPlan *plan) {
   if (!a_q || !a_scale || !w_q || !w_scale || !out) return W8A8_ERR_NULL;
   if (!gemm_shape_ok(M, N, K)) return W8A8_ERR_SHAPE;
   const int eb = out_elem_bytes(out_dtype);
@@ -119,24 +125,47 @@ int validate_gemm(const int8_t *a_q, const float *a_scale, const int8_t *w_q,
     return W8A8_ERR_ALIGN;
   *plan = w8a8::plan_gemm(M, N, K);
   if (!w8a8::plan_launchable(*plan)) return W8A8_ERR_SHAPE;
-  if (plan->workspace > 0) {
-    if (!workspace || workspace_bytes < plan->workspace)
-      return W8A8_ERR_WORKSPACE;
-    if (!aligned(workspace, 16)) return W8A8_ERR_ALIGN;
-  }
   const Range ro = range_of(out, M * N * eb);
   const Range ins[] = {range_of(a_q, M * K), range_of(a_scale, M * 4),
                        range_of(w_q, N * K), range_of(w_scale, N * 4),
                        range_of(bias, bias ? N * 2 : 0)};
   for (const Range &r : ins)
     if (overlap(ro, r)) return W8A8_ERR_ALIAS;
-  if (plan->workspace > 0) {
-    const Range rw = range_of(workspace, (int64_t)plan->workspace);
-    if (overlap(rw, ro)) return W8A8_ERR_ALIAS;
-    for (const Range &r : ins)
-      if (overlap(rw, r)) return W8A8_ERR_ALIAS;
-  }
   return W8A8_OK;
+}
+
+// The partial-sum buffer of a plan against the call's other buffers.
+int scratch_alias(const void *buf, const GemmPlan &plan, const int8_t *a_q,
+                  const float *a_scale, const int8_t *w_q,
+                  const float *w_scale, const uint16_t *bias,
+                  const void *out, int out_dtype, int64_t M, int64_t N,
+                  int64_t K) {
+  if (plan.workspace == 0) return W8A8_OK;
+  const Range rw = range_of(buf, (int64_t)plan.workspace);
+  const Range all[] = {range_of(out, M * N * out_elem_bytes(out_dtype)),
+                       range_of(a_q, M * K), range_of(a_scale, M * 4),
+                       range_of(w_q, N * K), range_of(w_scale, N * 4),
+                       range_of(bias, bias ? N * 2 : 0)};
+  for (const Range &r : all)
+    if (overlap(rw, r)) return W8A8_ERR_ALIAS;
+  return W8A8_OK;
+}
+
+int validate_gemm(const int8_t *a_q, const float *a_scale, const int8_t *w_q,
+                  const float *w_scale, const uint16_t *bias, const void *out,
+                  int out_dtype, int64_t M, int64_t N, int64_t K,
+                  const void *workspace, size_t workspace_bytes,
+                  GemmPlan *plan) {
+  int st = validate_gemm_args(a_q, a_scale, w_q, w_scale, bias, out,
+                              out_dtype, M, N, K, plan);
+  if (st != W8A8_OK) return st;
+  if (plan->workspace > 0) {
+    if (!workspace || workspace_bytes < plan->workspace)
+      return W8A8_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return W8A8_ERR_ALIGN;
+  }
+  return scratch_alias(workspace, *plan, a_q, a_scale, w_q, w_scale, bias,
+                       out, out_dtype, M, N, K);
 }
 
 }  // namespace
@@ -205,6 +234,37 @@ int w8a8_gemm(const int8_t *a_q, const float *a_scale, const int8_t *w_q,
   if ((st = check_device()) != W8A8_OK) return st;
   GemmArgs g{a_q, a_scale, w_q, w_scale, bias, out, out_dtype,
              M,   N,       K,   workspace, workspace_bytes};
+  return hip_status(
+      w8a8::launch_gemm(g, plan, static_cast<hipStream_t>(stream)));
+}
+
+int w8a8_gemm_noalloc(const int8_t *a_q, const float *a_scale,
+                      const int8_t *w_q, const float *w_scale,
+                      const uint16_t *bias, void *out, int out_dtype,
+                      int64_t M, int64_t N, int64_t K, void *stream) {
+  // As w8a8_gemm, with the split-K partial sums in the library's own device
+  // scratch (one copy per GPU) instead of a caller's workspace: nothing is
+  // allocated here.  A plan needing more than the scratch is refused (the
+  // planner's bound on partial sums makes that impossible today).
+  GemmPlan plan;
+  int st = validate_gemm_args(a_q, a_scale, w_q, w_scale, bias, out,
+                              out_dtype, M, N, K, &plan);
+  if (st != W8A8_OK) return st;
+  if (plan.workspace > w8a8::kScratchBytes) return W8A8_ERR_WORKSPACE;
+  if ((st = check_device()) != W8A8_OK) return st;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return W8A8_ERR_DEVICE;
+  void *scratch = w8a8::scratch_on_device(dev);
+  if (scratch == nullptr) {  // set-up failed at the device check: retry
+    st = hip_status(w8a8::resolve_scratch(dev));
+    if (st != W8A8_OK) return st;
+    scratch = w8a8::scratch_on_device(dev);
+  }
+  st = scratch_alias(scratch, plan, a_q, a_scale, w_q, w_scale, bias, out,
+                     out_dtype, M, N, K);
+  if (st != W8A8_OK) return st;
+  GemmArgs g{a_q, a_scale, w_q, w_scale, bias, out, out_dtype,
+             M,   N,       K,   scratch, w8a8::kScratchBytes};
   return hip_status(
       w8a8::launch_gemm(g, plan, static_cast<hipStream_t>(stream)));
 }
