@@ -101,13 +101,13 @@ def test_gemm_rejects(kw, code):
 
 
 def test_gemm_workspace_checks():
-    # M = 64 plans split-K and needs a workspace
-    need = B.gemm_workspace_bytes(64, 5376, 5376)
+    # M = 128 plans split-K over 64 x 128 tiles and needs a workspace
+    need = B.gemm_workspace_bytes(128, 5376, 5376)
     assert need > 0
-    assert gemm(M=64, N=5376, K=5376, ws=None, wsb=0) == WORKSPACE
-    assert gemm(M=64, N=5376, K=5376, wsb=need - 1) == WORKSPACE
-    assert gemm(M=64, N=5376, K=5376, ws=BUF["ws"] + 8, wsb=need) == ALIGN
-    assert gemm(M=64, N=5376, K=5376, ws=BUF["out"], wsb=need) == ALIAS
+    assert gemm(M=128, N=5376, K=5376, ws=None, wsb=0) == WORKSPACE
+    assert gemm(M=128, N=5376, K=5376, wsb=need - 1) == WORKSPACE
+    assert gemm(M=128, N=5376, K=5376, ws=BUF["ws"] + 8, wsb=need) == ALIGN
+    assert gemm(M=128, N=5376, K=5376, ws=BUF["out"], wsb=need) == ALIAS
 
 
 def test_gemm_accepts_planned_alignments():
@@ -118,8 +118,8 @@ def test_gemm_accepts_planned_alignments():
     if torch.cuda.device_count() > 0:
         pytest.skip("a GPU is present")
     assert gemm(sw=BUF["sw"] + 4, bias=BUF["bias"] + 2) == DEVICE
-    assert gemm(M=64, N=5376, K=5376, ws=BUF["ws"] + 16,
-                wsb=B.gemm_workspace_bytes(64, 5376, 5376)) == DEVICE
+    assert gemm(M=128, N=5376, K=5376, ws=BUF["ws"] + 16,
+                wsb=B.gemm_workspace_bytes(128, 5376, 5376)) == DEVICE
     assert linear(sw=BUF["sw"] + 12, bias=BUF["bias"] + 6,
                   ws=BUF["ws"] + 16) == DEVICE
     # K up to the INT32 bound through linear (the quantizer takes it too)
@@ -141,8 +141,15 @@ def test_workspace_sizes():
     assert g(4097, 4096, 1664) == 3 * 16 * tile    # 13 stages
     assert g(4097, 4096, 1024) == 2 * 16 * tile
     assert g(4097, 4096, 512) == 0            # 4 stages
-    ws = g(64, 5376, 5376)
-    assert ws % (64 * 5376 * 4) == 0 and ws // (64 * 5376 * 4) >= 2
+    # at most 64 tokens: one launch of the single-launch kernel, no partial
+    # sums; 65 to a few hundred tokens: 64 x 128 tiles split over K
+    for M in (1, 17, 32, 33, 64):
+        for N in (128, 5376, 16384):
+            assert g(M, N, 5376) == 0
+    assert g(64, 21504, 5376) == 0          # 168 tiles of 64 x 128, unsplit
+    assert g(64, 5376, 21504) > 0           # long K: split-K tiles
+    ws = g(128, 5376, 5376)
+    assert ws % (128 * 5376 * 4) == 0 and ws // (128 * 5376 * 4) >= 2
     assert g(64, 100, 5376) == 0  # rejected shape
     # w8a8_workspace_bytes: the codes and scales linear stages, each at a
     # 256-byte offset, plus the GEMM's partial sums (so it serves both)

@@ -285,6 +285,15 @@ def test_quantize_act_swiglu(orc, M, F):
 
 GEMM_SHAPES = [(1, 128, 128), (3, 384, 256), (64, 5376, 5376),
                (32, 128, 1280), (33, 384, 1152), (64, 256, 21504),
+               # at most 64 tokens, N and K at most 16384: one launch, the
+               # 8 waves taking one k-step each of every 256-byte stage
+               # (one or two token fragments; K an odd number of 128-byte
+               # halves leaves the last stage half full: 1152, 16256)
+               (48, 1152, 128), (64, 4096, 896), (64, 16384, 640),
+               (40, 2048, 16384), (60, 1024, 16256),
+               # few tokens past those bounds: 64 x 128 tiles split over K
+               (17, 21504, 384), (64, 16512, 640), (2, 384, 130944),
+               (128, 5376, 5376),
                (65, 256, 384), (257, 1280, 2048), (300, 384, 1152),
                (513, 768, 640), (1000, 640, 256),
                # a wave of 64x128 tiles, unsplit, 128-byte stages
@@ -403,8 +412,9 @@ def test_gemm_max_k_closed_form(M, N):
     # K at the INT32 bound: A[m, k] = a_m and W[n, k] = w_n with a_m, w_n
     # drawn from {-128, -127, -1, 0, 1, 127}, so acc[m, n] = a_m * w_n * K
     # exactly, up to 128 * 128 * 130944 = 2145386496 < 2^31.  Covers the
-    # split-K slices (M = 3, 300), the unsplit small tiles (1100) and the
-    # large tiles with a split tail (4097) over the longest K.
+    # single-launch kernel (M = 3), the split-K slices (300), the unsplit
+    # small tiles (1100) and the large tiles with a split tail (4097) over
+    # the longest K.
     K = B.MAX_K
     g = np.random.default_rng([11, M, N])
     vals = np.array([-128, -127, -1, 0, 1, 127], np.int64)
@@ -460,12 +470,14 @@ def test_gemm_tail_split(orc, M, N, K):
     assert np.array_equal(yb, rb)
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 5376, 5376), (4097, 4096, 1024)])
+@pytest.mark.parametrize("M,N,K", [(64, 5376, 5376), (128, 5376, 5376),
+                                   (4097, 4096, 1024)])
 def test_graph_replay(orc, M, N, K):
     # The library enqueues kernel launches only (no memsets, no host waits),
     # so a HIP graph of quantize + GEMM + SiLU-quantize replays the eager
-    # results bit for bit.  M=64 takes the skinny split-K path and its
-    # reduction; 4097 x 4096 the tail split and tail reduction.  Outputs are
+    # results bit for bit.  M=64 takes the single-launch kernel, M=128 the
+    # split-K path and its reduction; 4097 x 4096 the tail split and tail
+    # reduction.  Outputs are
     # overwritten with a pattern before every replay, and eager library
     # calls on other buffers run between the replays.
     say(f"graph replay M={M} N={N} K={K}")
@@ -579,7 +591,8 @@ def test_gemm_epilogue_edge_values(orc):
     negative values; rows carry the accumulator (row m of A has acc[m]
     entries equal to +-1, every weight is 1), columns the weight scale and
     bias.  Checked exactly against the oracle on every (row, column) pair,
-    through both the staged large-M kernel and the skinny split-K path."""
+    through the staged large-M kernel, the split-K path and the
+    single-launch kernel."""
     K = 1152
     accs = [257, 258, 259, -257, 0, 1, -1, 1000, 1024, K, -K, 3, 515, 771]
     sas = [1.0, 1.0, 1.0, 1.0, 1.0, 2.0 ** -140, 2.0 ** -140, 0.5, 2.0 ** -126,
@@ -588,7 +601,9 @@ def test_gemm_epilogue_edge_values(orc):
     biases = [0.0, 0.5, -0.25, 0.0, 2.0 ** -133, 1.0] * 43
     N = 256
     sws, biases = sws[:N], biases[:N]
-    for M in (300, 14):   # 300 rows: large-M kernel; 14 rows: split-K path
+    # 300 rows: large-M kernel; 100 rows: split-K over 64 x 128 tiles;
+    # 14 rows: the single-launch kernel
+    for M in (300, 100, 14):
         say(f"gemm epilogue edge values M={M} N={N} K={K}")
         a = np.zeros((M, K), np.int8)
         sa = np.zeros(M, np.float32)
@@ -637,16 +652,17 @@ def test_binding_rejects_mismatched_outputs():
 # boundary cases: tile addresses, argument alignment, side streams
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("M,N,K", [(4097, 4096, 1024), (64, 5376, 5376),
-                                   (1100, 2048, 896)])
+@pytest.mark.parametrize("M,N,K", [(4097, 4096, 1024), (128, 5376, 5376),
+                                   (64, 5376, 5376), (1100, 2048, 896)])
 def test_gemm_tile_bases_across_bit31(orc, M, N, K):
     """Operands placed in one device buffer so that A crosses an address
     whose low 32 bits are 0x80000000 in the middle of its rows and W lies
     just above it: many tiles' base addresses then have bit 31 of the low
     word set (a buffer resource built from a sign-extended low word would
     read from a wrong address).  Through the large-tile launch with its
-    split tail (4097), the split-K skinny launch (64) and the unsplit small
-    tiles (1100); accumulators and BF16 outputs against the oracle."""
+    split tail (4097), the split-K launch of 64 x 128 tiles (128), the
+    single-launch kernel (64) and the unsplit small tiles (1100);
+    accumulators and BF16 outputs against the oracle."""
     say(f"gemm tile bases across bit 31 M={M} N={N} K={K}")
     a, w, sa, sw, bias = gemm_inputs(M, N, K, 31)
     buf = torch.empty(((1 << 32) + M * K + N * K + 4096,), dtype=torch.uint8,
@@ -677,7 +693,8 @@ def test_gemm_tile_bases_across_bit31(orc, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 384, 640), (4097, 4096, 1024),
-                                   (64, 5376, 5376), (1100, 2048, 896)])
+                                   (64, 5376, 5376), (128, 5376, 5376),
+                                   (1100, 2048, 896)])
 def test_gemm_unaligned_scale_and_bias(orc, M, N, K):
     """Channel scales only 4-byte aligned and biases only 2-byte aligned
     (one element into larger arrays), through every launch path; BF16 and

@@ -40,7 +40,7 @@ def guarded(M, N, dtype):
 # First a large-tile shape with a split tail (partial sums of 48 tail-tile
 # slices in the scratch), then a smaller skinny shape (split-K over the
 # whole output), then a shape with no split at all.
-SHAPES = [(4097, 4096, 1664), (64, 5376, 5376), (300, 384, 640)]
+SHAPES = [(4097, 4096, 1664), (128, 5376, 5376), (300, 384, 640)]
 
 
 def test_noalloc_equals_gemm_on_consecutive_calls():

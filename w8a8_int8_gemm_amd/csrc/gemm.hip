@@ -692,6 +692,200 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Single-launch GEMM for at most 64 tokens
+// ---------------------------------------------------------------------------
+// With so few tokens the weights dominate the bytes (M = 64, K = N = 5376:
+// 28.9 MB of 30 MB) and the call is bound by streaming them from HBM.  Each
+// work group owns all tokens and 32 output channels over the whole K, so
+// no partial sums leave the work group and one launch does the call:
+//   * K is staged 256 bytes at a time (8 k-steps of 32 bytes) through a ring
+//     of NS LDS slots filled by direct loads (each 1 KiB load instruction
+//     covers 4 whole rows of the stage);
+//   * wave w of the 8 computes k-step w of every stage: it reads its token
+//     and weight fragments from the slot and issues TM MFMAs, so the waves
+//     split K and nothing is shared between them but the staging;
+//   * the waves' INT32 sums meet in LDS once the ring is drained, and all
+//     threads finish the call: 4 outputs each, summed over the 8 waves,
+//     then the same epilogue as the tiled kernels.
+// Token rows past M are loaded from row M - 1 and never stored.  When K is
+// an odd number of 128-byte halves the last stage is half full: its missing
+// columns are loaded from the row's last 16 bytes (in bounds) and the waves
+// whose k-step lies there skip it.
+constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyThreads = kSkinnyWaves * 64;
+#ifndef W8A8_SKINNY_NS
+#define W8A8_SKINNY_NS 4
+#endif
+
+template <int TM>
+struct SkinnyCfg {
+  static constexpr int BK = 256;                 // K bytes per stage
+  static constexpr int CPR = BK / 16;            // 16-byte chunks per row
+  static constexpr int A_ROWS = 32 * TM;         // token rows staged
+  static constexpr int B_ROWS = 32;              // channel rows staged
+  static constexpr int STAGE = (A_ROWS + B_ROWS) * BK;
+  static constexpr int NS = W8A8_SKINNY_NS;
+  static constexpr int LOADS = STAGE / (1024 * kSkinnyWaves);  // per wave
+  static constexpr int LDS = NS * STAGE;
+  // cross-wave sums: per wave 32*TM tokens x 32 channels of INT32, rows
+  // padded by 4 ints so 16-byte stores of 32 rows spread over the banks
+  static constexpr int ROW = 32 + 4;
+  static constexpr int WAVE = 32 * TM * ROW;
+  static_assert(STAGE % (1024 * kSkinnyWaves) == 0, "whole loads per wave");
+  static_assert(kSkinnyWaves * WAVE * 4 <= LDS, "sums fit in the ring");
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+// Position of logical 16-byte chunk c in staged row r (16 chunks per row):
+// the 16 lanes that one LDS cycle serves read 16 different rows at one
+// logical chunk, which land on 16 different physical chunks.
+__device__ __forceinline__ int swz16(int r, int c) { return c ^ (r & 15); }
+
+template <int TM, int EPI>
+__global__ __launch_bounds__(kSkinnyThreads, 1) void skinny_kernel(
+    KernelArgs p) {
+  using C = SkinnyCfg<TM>;
+  extern __shared__ __attribute__((aligned(1024))) int8_t smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * 32;
+  const int halves = p.K / 128;
+  const int nst = (halves + 1) / 2;  // stages (the last may be half)
+
+  // Direct loads: instruction j of this wave fills 1 KiB block
+  // b = j * 8 + wave of a stage: token rows 4b .. 4b + 3, or, past the
+  // token rows, channel rows.  Lane i writes row 4b + i / 16 at physical
+  // chunk i mod 16, which holds logical chunk swz16(row, i mod 16).
+  int rowoff[C::LOADS], chunk[C::LOADS];
+  bool is_w[C::LOADS];
+#pragma unroll
+  for (int j = 0; j < C::LOADS; ++j) {
+    const int b = j * kSkinnyWaves + wave;
+    const int r = b * 4 + lane / 16;  // staged row
+    is_w[j] = r >= C::A_ROWS;
+    // rows relative to the operand's resource base: tokens from row 0,
+    // weights from this work group's first channel (offsets stay below
+    // 64 * W8A8_MAX_K)
+    const int grow = is_w[j] ? r - C::A_ROWS : min(r, p.M - 1);
+    rowoff[j] = grow * p.K;
+    chunk[j] = swz16(r, lane & 15) * 16;
+  }
+  const auto ra = tile_rsrc(p.a);
+  const auto rw = tile_rsrc(p.w + (int64_t)n0 * p.K);
+  auto issue = [&](int slot, int st) {
+    int8_t *base = smem + slot * C::STAGE;
+    const int s0 = min(st, nst - 1) * C::BK;
+#pragma unroll
+    for (int j = 0; j < C::LOADS; ++j) {
+      const int col = min(s0 + chunk[j], p.K - 16);
+      load_lds16(is_w[j] ? rw : ra, rowoff[j] + col, 0,
+                 (lds_void *)(base + (j * kSkinnyWaves + wave) * 1024));
+    }
+  };
+
+  // Fragment reads of this wave's k-step: lane reads row (lane mod 32) of a
+  // 32-row fragment, logical chunk 2 wave + lane / 32.
+  const int fr = lane & 31;
+  const int lc = 2 * wave + (lane >> 5);
+  int xoff[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+    xoff[i] = (i * 32 + fr) * C::BK + swz16(i * 32 + fr, lc) * 16;
+  const int woff =
+      (C::A_ROWS + fr) * C::BK + swz16(C::A_ROWS + fr, lc) * 16;
+  const bool last_half = (halves & 1) != 0;
+
+  v16i acc[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0;
+
+  // Ring: stages 0 .. NS-2 requested up front (a stage past the end
+  // reloads the last one, so every step issues the same loads); at stage kt
+  // the wave waits for its loads of stage kt, all waves meet (every load of
+  // stage kt has landed; every read of stage kt-1 is done), stage
+  // kt + NS - 1 goes into stage kt-1's slot, then the wave's k-step.
+#pragma unroll
+  for (int st = 0; st < C::NS - 1; ++st) issue(st, st);
+  for (int kt = 0; kt < nst; ++kt) {
+    wait_vmcnt<(C::NS - 2) * C::LOADS>();
+    wait_lgkm<0>();
+    block_barrier();
+    issue((kt + C::NS - 1) % C::NS, kt + C::NS - 1);
+    const int8_t *slot = smem + (kt % C::NS) * C::STAGE;
+    if (!(last_half && kt == nst - 1 && wave >= 4)) {
+      const v4i wf = read_lds16(slot, woff);
+      v4i xf[TM];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) xf[i] = read_lds16(slot, xoff[i]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf, xf[i], acc[i], 0,
+                                                       0, 0);
+    }
+  }
+  wait_vmcnt<0>();  // the drain copies have landed before the ring is reused
+  wait_lgkm<0>();
+  block_barrier();
+
+  // Each wave's sums, [token][channel] in its LDS region: register 4g + t of
+  // accumulator i holds token 32 i + (lane mod 32) and channel
+  // 8 g + 4 (lane / 32) + t.
+  int *red = reinterpret_cast<int *>(smem);
+  int *mine = red + wave * C::WAVE;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int m = i * 32 + fr;
+      const int c = 8 * g + 4 * (lane >> 5);
+      *reinterpret_cast<v4i *>(mine + m * C::ROW + c) =
+          v4i{acc[i][4 * g], acc[i][4 * g + 1], acc[i][4 * g + 2],
+              acc[i][4 * g + 3]};
+    }
+  __syncthreads();
+
+  // Four outputs per thread: token m, channels c .. c + 3.
+  for (int q = threadIdx.x; q < 32 * TM * 8; q += kSkinnyThreads) {
+    const int m = q / 8, c = (q % 8) * 4;
+    v4i s = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int w = 0; w < kSkinnyWaves; ++w)
+      s += *reinterpret_cast<const v4i *>(red + w * C::WAVE + m * C::ROW + c);
+    if (m >= p.M) continue;
+    const int nn = n0 + c;
+    const int64_t o = (int64_t)m * p.N + nn;
+    if (EPI == EPI_I32) {
+      *reinterpret_cast<v4i *>(static_cast<int *>(p.out) + o) = s;
+      continue;
+    }
+    const float sam = p.sa[m];
+    const float4 swn = load_scale4(p.sw, nn, p.vec_sw);
+    float t0 = ((float)s.x * sam) * swn.x;
+    float t1 = ((float)s.y * sam) * swn.y;
+    float t2 = ((float)s.z * sam) * swn.z;
+    float t3 = ((float)s.w * sam) * swn.w;
+    if (p.bias) {
+      const float4 bv = load_bias4(p.bias, nn, p.vec_bias);
+      t0 = t0 + bv.x;
+      t1 = t1 + bv.y;
+      t2 = t2 + bv.z;
+      t3 = t3 + bv.w;
+    }
+    if (EPI == EPI_FP32) {
+      *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + o) =
+          make_float4(t0, t1, t2, t3);
+    } else {
+      uint2 v;
+      v.x = pack_bf16x2(t0, t1);
+      v.y = pack_bf16x2(t2, t3);
+      *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.out) + o) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Tile configurations
 // ---------------------------------------------------------------------------
 // Large M: 256x256 tiles, 8 waves (two per SIMD) of 64x128, two slots of
@@ -857,7 +1051,76 @@ hipError_t set_lds_limit() {
 constexpr int kCfgLarge = 0;
 constexpr int kCfgSkinny = 1;
 constexpr int kCfgMid = 2;
+constexpr int kCfgSingle = 3;  // skinny_kernel: at most 64 tokens, one launch
 constexpr int kCUs = 256;
+
+template <int TM>
+hipError_t set_skinny_lds() {
+  hipError_t e = hipSuccess;
+  constexpr int lds = SkinnyCfg<TM>::LDS;
+  if (lds > 64 * 1024) {
+    e = hipFuncSetAttribute((const void *)skinny_kernel<TM, EPI_BF16>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void *)skinny_kernel<TM, EPI_FP32>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void *)skinny_kernel<TM, EPI_I32>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  }
+  return e;
+}
+
+// Dynamic LDS above 64 KiB, opted in once per device (result kept).
+template <int TM>
+hipError_t ensure_skinny_lds() {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::unordered_map<int, hipError_t> done;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = done.find(dev);
+  if (it != done.end()) return it->second;
+  const hipError_t r = set_skinny_lds<TM>();
+  done[dev] = r;
+  return r;
+}
+
+template <int TM>
+hipError_t launch_skinny(const GemmArgs &g, hipStream_t stream) {
+  const hipError_t lds_ok = ensure_skinny_lds<TM>();
+  if (lds_ok != hipSuccess) return lds_ok;
+  KernelArgs p{};
+  p.a = g.a;
+  p.sa = g.sa;
+  p.w = g.w;
+  p.sw = g.sw;
+  p.bias = g.bias;
+  p.out = g.out;
+  p.M = (int)g.M;
+  p.N = (int)g.N;
+  p.K = (int)g.K;
+  p.vec_sw = (reinterpret_cast<uintptr_t>(g.sw) & 15) == 0;
+  p.vec_bias = (reinterpret_cast<uintptr_t>(g.bias) & 7) == 0;
+  const dim3 grid((unsigned)(g.N / 32));
+  constexpr int lds = SkinnyCfg<TM>::LDS;
+  switch (g.epi) {
+    case EPI_BF16:
+      hipLaunchKernelGGL((skinny_kernel<TM, EPI_BF16>), grid,
+                         dim3(kSkinnyThreads), lds, stream, p);
+      break;
+    case EPI_FP32:
+      hipLaunchKernelGGL((skinny_kernel<TM, EPI_FP32>), grid,
+                         dim3(kSkinnyThreads), lds, stream, p);
+      break;
+    default:
+      hipLaunchKernelGGL((skinny_kernel<TM, EPI_I32>), grid,
+                         dim3(kSkinnyThreads), lds, stream, p);
+      break;
+  }
+  return hipGetLastError();
+}
 
 // Token tiles per group of the tile order: a narrow output (few channel
 // tiles) affords taller groups within one wave of work groups.
@@ -887,6 +1150,12 @@ constexpr int kCUs = 256;
 // large-tile time then beats the small tiles (measured at N=5376, K=5376:
 // M=1280, 105 large tiles, 61 us against 81 us of small tiles; M=1024, 84
 // large tiles, small tiles win with 55 us).
+#ifndef W8A8_SINGLE_MAX_N
+#define W8A8_SINGLE_MAX_N 16384
+#endif
+#ifndef W8A8_SINGLE_MAX_K
+#define W8A8_SINGLE_MAX_K 16384
+#endif
 #ifndef W8A8_LARGE_MIN_TILES
 #define W8A8_LARGE_MIN_TILES 112
 #endif
@@ -931,7 +1200,18 @@ void *scratch_on_device(int device) {
 }
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
-  GemmPlan plan{kCfgLarge, 1, CfgLarge::GROUP_M, 0, 0, 0, 0};
+  GemmPlan plan{kCfgLarge, 1, CfgLarge::GROUP_M, 0, 0, 0, 0, 0};
+  // At most 64 tokens: one launch, no partial sums (skinny_kernel), while
+  // its N / 32 work groups stay within two per CU and K within 16384
+  // (measured at M = 64, against the split-K tiles below: N = K = 5376
+  // 7.9 against 12.0 us, N = 16128 19.1 against 20.0 us; N = 21504 25.8
+  // against 19.7 us, K = 21504 25.2 against 24.4 us).
+  if (M <= 64 && N <= W8A8_SINGLE_MAX_N && K <= W8A8_SINGLE_MAX_K) {
+    plan.config = kCfgSingle;
+    plan.skinny_tm = M <= 32 ? 1 : 2;
+    plan.main_tiles = (int)(N / 32);
+    return plan;
+  }
   const int64_t tiles_n = (N + CfgLarge::BN - 1) / CfgLarge::BN;
   plan.group_m = tiles_n <= 32 ? W8A8_GROUP_M_NARROW : W8A8_GROUP_M_WIDE;
   const int64_t large_tiles = ((M + CfgLarge::BM - 1) / CfgLarge::BM) * tiles_n;
@@ -985,9 +1265,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
 bool plan_launchable(const GemmPlan &plan) {
   // A launch holds fewer than 2^32 work-items per grid dimension.
   const uint64_t lim = 0xFFFFFFFFull;
-  const uint64_t threads = plan.config == kCfgLarge  ? CfgLarge::THREADS
-                           : plan.config == kCfgMid ? CfgMid::THREADS
-                                                    : CfgSkinny::THREADS;
+  const uint64_t threads = plan.config == kCfgLarge    ? CfgLarge::THREADS
+                           : plan.config == kCfgMid    ? CfgMid::THREADS
+                           : plan.config == kCfgSingle ? kSkinnyThreads
+                                                       : CfgSkinny::THREADS;
   if ((uint64_t)plan.main_tiles * threads > lim) return false;
   if ((uint64_t)plan.tail_tiles * threads > lim) return false;
   return (uint64_t)plan.tail_tiles * (CfgLarge::BM * CfgLarge::BN / 4) <= lim;
@@ -997,6 +1278,9 @@ hipError_t launch_gemm(const GemmArgs &args, const GemmPlan &plan,
                        hipStream_t stream) {
   if (plan.config == kCfgLarge) return launch_cfg<CfgLarge>(args, plan, stream);
   if (plan.config == kCfgMid) return launch_cfg<CfgMid>(args, plan, stream);
+  if (plan.config == kCfgSingle)
+    return plan.skinny_tm == 1 ? launch_skinny<1>(args, stream)
+                               : launch_skinny<2>(args, stream);
   return launch_cfg<CfgSkinny>(args, plan, stream);
 }
 

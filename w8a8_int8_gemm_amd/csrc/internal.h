@@ -129,6 +129,7 @@ struct GemmPlan {
   int tail_tiles;    // trailing tiles run split-K in a second launch
   int tail_splits;   // K slices per tail tile (0 = no tail launch)
   size_t workspace;  // bytes of INT32 partials needed (0 if none)
+  int skinny_tm;     // single-launch skinny kernel: token fragments (1, 2)
 };
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
