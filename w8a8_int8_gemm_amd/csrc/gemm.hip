@@ -1276,6 +1276,12 @@ bool plan_launchable(const GemmPlan &plan) {
 
 hipError_t launch_gemm(const GemmArgs &args, const GemmPlan &plan,
                        hipStream_t stream) {
+  // The partial sums of a split plan go to the workspace: refuse to launch
+  // without one of the planned size (the API layer checks this first; this
+  // guards direct callers of the launcher).
+  if (plan.workspace > 0 &&
+      (args.workspace == nullptr || args.workspace_bytes < plan.workspace))
+    return hipErrorInvalidValue;
   if (plan.config == kCfgLarge) return launch_cfg<CfgLarge>(args, plan, stream);
   if (plan.config == kCfgMid) return launch_cfg<CfgMid>(args, plan, stream);
   if (plan.config == kCfgSingle)
