@@ -281,6 +281,32 @@ def test_build_id_matches_sources(monkeypatch):
         B.lib()
 
 
+def test_library_shares_torchs_hip_runtime():
+    """torch's ROCm build carries its own HIP and HSA runtimes.  The binding
+    loads the library after torch, so the library's HIP symbols resolve to
+    torch's runtime; loaded first (as a stale-build check before any torch
+    import once did), it would bring in the system runtime beside torch's,
+    and on a GPU the library then saw no device.  In a fresh process:
+    exactly one HIP and one HSA runtime are mapped, whatever loads first."""
+    import subprocess
+    import sys
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "from w8a8_int8_gemm_amd import binding as B\n"
+        "B.build_is_stale(); B.lib()\n"
+        "import torch; torch.zeros(1)\n"
+        "maps = open('/proc/self/maps').read().splitlines()\n"
+        "for key in ('libamdhip64', 'libhsa-runtime64'):\n"
+        "    print(key, sorted({l.split()[-1] for l in maps if key in l}))\n"
+    ) % str(ROOT)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    for line in r.stdout.splitlines():
+        key, paths = line.split(" ", 1)
+        assert len(eval(paths)) == 1, line  # one runtime of each kind
+
+
 def test_binding_checks_tensors_before_calling():
     """The wrappers check dtype, shape and device of every tensor before a
     pointer reaches the C ABI (CPU tensors here: refused as not on a GPU)."""

@@ -62,6 +62,12 @@ _lib = None
 
 
 def _load(path):
+    # torch first: its ROCm build carries its own HIP runtime, and the
+    # library must resolve its HIP symbols to that same runtime (found by
+    # its soname once loaded).  Loaded before torch, the library would pull
+    # in the system HIP runtime and torch would then load a second one; the
+    # library's device calls then fail (no device is visible to it).
+    import torch  # noqa: F401
     L = ctypes.CDLL(str(path))
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(L, name)
