@@ -35,7 +35,8 @@ Inputs and weights are resident in HBM before timing starts.  Reported:
   measured_peaks (context) = a device copy's HBM rate and torch's BF16 GEMM
                rate on this box, beside the published peaks;
   bf16_baseline (context) = torch's BF16 linear (hipBLASLt) on the same
-               shapes;
+               shapes, and how many times faster the W8A8 step runs a
+               block (w8a8_speedup);
   int8_library_baseline (context) = hipBLASLt's INT8 GEMM (torch._int_mm)
                on the same codes and weights: INT32 accumulators only, no
                scales, bias or BF16 rounding;
@@ -668,7 +669,9 @@ def run(args, sampler):
     if not args.no_bf16_baseline:
         bf16 = bf16_baseline(torch, wl, w.x0, w.blocks[0],
                              args.warmup, max(args.steps, 3))
-        log(f"[bench] BF16 baseline: {bf16['tflops']:.1f} TFLOPS")
+        bf16["w8a8_speedup"] = speedup_vs_bf16(bf16, m["ms_step"], wl.blocks)
+        log(f"[bench] BF16 baseline: {bf16['tflops']:.1f} TFLOPS (the W8A8 "
+            f"step {bf16['w8a8_speedup']:.3f}x faster per block)")
     int8lib = None
     if not args.no_int8_library_baseline:
         codes = ({wl.projs[0].name: w.qbuf} if w.single
@@ -922,6 +925,12 @@ def kernel_source_sha256():
     for name in ("gemm.hip", "internal.h"):
         h.update((csrc / name).read_bytes())
     return h.hexdigest()
+
+
+def speedup_vs_bf16(bf16, ms_step, blocks):
+    """How many times faster the W8A8 step runs one block (quantizations,
+    GEMMs and glue) than the BF16 baseline runs the same block."""
+    return round(bf16["ms_per_block"] / (ms_step / blocks), 3)
 
 
 def bf16_baseline(torch, wl, x0, blk, warmup, reps):

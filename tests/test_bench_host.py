@@ -133,3 +133,8 @@ def test_power_clock_sampler_parses_amd_smi_json(tmp_path):
     assert w["gfx_clock_mhz_min_mean_max"] == [1700, 1704, 1707]
     assert w["xcds"] == 8
     assert s.window(20, 30) is None
+
+
+def test_speedup_vs_bf16_is_per_block():
+    # 50 blocks in 300 ms against a BF16 block of 10.2 ms: 1.7x per block
+    assert bench.speedup_vs_bf16({"ms_per_block": 10.2}, 300.0, 50) == 1.7
