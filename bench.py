@@ -52,6 +52,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import shutil
 import signal
@@ -71,12 +72,16 @@ INT8_PEAK_TOPS = 5000.0   # MI355X dense INT8 MFMA, published
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
 GRAPH_GEMM_REPEATS = 20   # GEMM calls per timing graph (single projection)
 GRAPH_STAT_REPLAYS = 7    # replays of the step graph for the median / std
-# A spin kernel of this many GPU clock cycles (tens of milliseconds) is
-# queued ahead of each eager timed region: the host then enqueues the
-# region's launches and events before the GPU reaches them, so no event
-# pair spans a pause of the host (short calls of the one-block workloads
-# otherwise let the GPU drain between launches).
+# Untimed work queued ahead of each eager timed region: the host then
+# enqueues the region's launches and events before the GPU reaches them, so
+# no event pair spans a pause of the host (short calls of the one-block
+# workloads otherwise let the GPU drain between launches).  By default that
+# work is steps of the workload itself, about LEAD_MS of them (the GPU stays
+# at its working clock up to the first timed step); with --lead spin, a spin
+# kernel of QUEUE_AHEAD_CYCLES GPU clock cycles.
 QUEUE_AHEAD_CYCLES = 100_000_000
+LEAD_MS = 50.0
+LEAD_MAX_STEPS = 64
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 MFMA, published
 PER_CONFIGS = (0, 1, 2, 3)  # single-GPU workloads reported beside the main
 METRIC = ("W8A8 projection TOPS and % INT8 MFMA peak at DiT shapes "
@@ -122,6 +127,10 @@ def parse(argv=None):
                          "HIP graph; auto = on for the single-projection "
                          "workload, whose kernels are shorter than the "
                          "Python launch path")
+    ap.add_argument("--lead", choices=("steps", "spin"), default="steps",
+                    help="untimed work queued right before each eager timed "
+                         "region while the host enqueues it: steps of the "
+                         "workload (default) or a bounded spin kernel")
     ap.add_argument("--traffic-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 4 times (a kernel "
                          "of known HBM traffic for scaling rocprofv3's "
@@ -263,7 +272,8 @@ def quant_bytes(kind, M, K):
 class Workload:
     """One workload of datagen.WORKLOADS, resident on the device."""
 
-    def __init__(self, wl, dev, qkv, check_rows, orc, threads, graph):
+    def __init__(self, wl, dev, qkv, check_rows, orc, threads, graph,
+                 lead="steps"):
         import torch
         from w8a8_int8_gemm_amd import binding as B
         from w8a8_int8_gemm_amd import block as BL
@@ -322,6 +332,7 @@ class Workload:
                                          o_input=wl.o_input)
         self.ops_per_step = sum(2 * M * p.N * p.K for blk in self.blocks
                                 for p in blk.values())
+        self.lead, self.lead_steps = lead, 1
 
     # -- one step ------------------------------------------------------------
     def step(self, on_gemm=None, on_quant=None, on_block=None):
@@ -364,9 +375,30 @@ class Workload:
         return out
 
     def warmup(self, n):
+        torch = self.torch
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
         for _ in range(n):
             self.step()
-        self.torch.cuda.synchronize()
+        e1.record()
+        torch.cuda.synchronize()
+        # steps run ahead of each eager timed region (untimed), enough to
+        # keep the GPU busy for LEAD_MS while the host enqueues the region
+        est = e0.elapsed_time(e1) / max(n, 1)
+        self.lead_steps = max(1, min(LEAD_MAX_STEPS,
+                                     math.ceil(LEAD_MS / max(est, 1e-3))))
+
+    def lead_in(self):
+        """Untimed work queued right before an eager timed region, so that
+        the host enqueues the region's launches and events while the GPU is
+        busy: real steps (the GPU stays at its working clock), or with
+        ``--lead spin`` a bounded spin kernel."""
+        if self.lead == "spin":
+            self.torch.cuda._sleep(QUEUE_AHEAD_CYCLES)
+            return
+        for _ in range(self.lead_steps):
+            self.step()
 
     # -- timed region 1: whole steps -------------------------------------------
     def time_steps(self, K):
@@ -398,7 +430,7 @@ class Workload:
                 f"{GRAPH_STAT_REPLAYS} times (value from the first)"
         evs = [Ev() for _ in range(K + 1)]
         torch.cuda.synchronize()
-        torch.cuda._sleep(QUEUE_AHEAD_CYCLES)
+        self.lead_in()
         evs[0].record()
         for i in range(K):
             self.step()
@@ -472,7 +504,7 @@ class Workload:
             return f
 
         torch.cuda.synchronize()
-        torch.cuda._sleep(QUEUE_AHEAD_CYCLES)
+        self.lead_in()
         for _ in range(K):
             self.step(on_gemm=hook("gemm"), on_quant=hook("quant"))
         torch.cuda.synchronize()
@@ -646,7 +678,7 @@ def run(args, sampler):
         orc = oracle.default()
     wl = D.WORKLOADS[args.config]
     w = Workload(wl, dev, args.qkv, 0 if args.no_check else args.check_rows,
-                 orc, threads, args.graph)
+                 orc, threads, args.graph, args.lead)
     m = measure(w, args.steps, args.warmup, sampler)
     log(f"[bench] step {m['ms_step']:.3f} ms -> {m['tops']:.1f} TOPS "
         f"({100 * m['tops'] / INT8_PEAK_TOPS:.1f}% of INT8 peak); GEMM calls "
@@ -763,7 +795,7 @@ def run(args, sampler):
 def per_config_entry(wl, dev, orc, threads, args):
     """A compact entry for another workload: value, step statistics, the
     GEMM call's roofline, per-phase rates and its own oracle check."""
-    w = Workload(wl, dev, "auto", 8, orc, threads, "auto")
+    w = Workload(wl, dev, "auto", 8, orc, threads, "auto", args.lead)
     m = measure(w, args.per_config_steps, 2)
     check = w.check()
     r = roofline_entry(w.blocks[0], w.M, m["gemm_tops"], m["avg_launch_us"],
