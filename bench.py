@@ -78,10 +78,12 @@ GRAPH_STAT_REPLAYS = 7    # replays of the step graph for the median / std
 # workloads otherwise let the GPU drain between launches).  By default that
 # work is steps of the workload itself, about LEAD_MS of them (the GPU stays
 # at its working clock up to the first timed step); with --lead spin, a spin
-# kernel of QUEUE_AHEAD_CYCLES GPU clock cycles.
+# kernel of QUEUE_AHEAD_CYCLES GPU clock cycles.  Timed graph replays are
+# led the same way by about LEAD_MS of replays of the same graph.
 QUEUE_AHEAD_CYCLES = 100_000_000
 LEAD_MS = 50.0
 LEAD_MAX_STEPS = 64
+LEAD_MAX_REPLAYS = 1024
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 MFMA, published
 PER_CONFIGS = (0, 1, 2, 3)  # single-GPU workloads reported beside the main
 METRIC = ("W8A8 projection TOPS and % INT8 MFMA peak at DiT shapes "
@@ -389,6 +391,21 @@ class Workload:
         self.lead_steps = max(1, min(LEAD_MAX_STEPS,
                                      math.ceil(LEAD_MS / max(est, 1e-3))))
 
+    def graph_lead_in(self, g):
+        """Replays of graph ``g`` queued right before its timed replays
+        (about LEAD_MS of them, at least one), from a timed warm replay."""
+        torch = self.torch
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        n = max(1, min(LEAD_MAX_REPLAYS, math.ceil(
+            LEAD_MS / max(e0.elapsed_time(e1), 1e-3))))
+        for _ in range(n):
+            g.replay()
+
     def lead_in(self):
         """Untimed work queued right before an eager timed region, so that
         the host enqueues the region's launches and events while the GPU is
@@ -417,7 +434,7 @@ class Workload:
             g.replay()
             torch.cuda.synchronize()
             evs = [Ev() for _ in range(GRAPH_STAT_REPLAYS + 1)]
-            torch.cuda.synchronize()
+            self.graph_lead_in(g)
             evs[0].record()
             for i in range(GRAPH_STAT_REPLAYS):
                 g.replay()
@@ -473,6 +490,7 @@ class Workload:
                 torch.cuda.synchronize()
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
+                self.graph_lead_in(g)
                 e0.record()
                 for _ in range(K):
                     g.replay()
