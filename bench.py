@@ -76,13 +76,15 @@ GRAPH_STAT_REPLAYS = 7    # replays of the step graph for the median / std
 # enqueues the region's launches and events before the GPU reaches them, so
 # no event pair spans a pause of the host (short calls of the one-block
 # workloads otherwise let the GPU drain between launches).  By default that
-# work is steps of the workload itself, about LEAD_MS of them (the GPU stays
-# at its working clock up to the first timed step); with --lead spin, a spin
-# kernel of QUEUE_AHEAD_CYCLES GPU clock cycles.  Timed graph replays are
-# led the same way by about LEAD_MS of replays of the same graph.
+# work is steps of the workload itself, about LEAD_MS of them: after the
+# host synchronization before a region the board's clock takes a few
+# hundred milliseconds of load to settle, so the region starts at the clock
+# the workload runs at when it runs continuously.  With --lead spin it is a
+# spin kernel of QUEUE_AHEAD_CYCLES GPU clock cycles instead.  Timed graph
+# replays are led the same way by about LEAD_MS of replays of the graph.
 QUEUE_AHEAD_CYCLES = 100_000_000
-LEAD_MS = 50.0
-LEAD_MAX_STEPS = 64
+LEAD_MS = 500.0
+LEAD_MAX_STEPS = 1000
 LEAD_MAX_REPLAYS = 1024
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 MFMA, published
 PER_CONFIGS = (0, 1, 2, 3)  # single-GPU workloads reported beside the main
@@ -129,6 +131,9 @@ def parse(argv=None):
                          "HIP graph; auto = on for the single-projection "
                          "workload, whose kernels are shorter than the "
                          "Python launch path")
+    ap.add_argument("--lead-ms", type=float, default=LEAD_MS,
+                    help="milliseconds of untimed steps (or graph replays) "
+                         "queued ahead of each timed region")
     ap.add_argument("--lead", choices=("steps", "spin"), default="steps",
                     help="untimed work queued right before each eager timed "
                          "region while the host enqueues it: steps of the "
@@ -275,7 +280,7 @@ class Workload:
     """One workload of datagen.WORKLOADS, resident on the device."""
 
     def __init__(self, wl, dev, qkv, check_rows, orc, threads, graph,
-                 lead="steps"):
+                 lead="steps", lead_ms=LEAD_MS):
         import torch
         from w8a8_int8_gemm_amd import binding as B
         from w8a8_int8_gemm_amd import block as BL
@@ -334,7 +339,7 @@ class Workload:
                                          o_input=wl.o_input)
         self.ops_per_step = sum(2 * M * p.N * p.K for blk in self.blocks
                                 for p in blk.values())
-        self.lead, self.lead_steps = lead, 1
+        self.lead, self.lead_steps, self.lead_ms = lead, 1, lead_ms
 
     # -- one step ------------------------------------------------------------
     def step(self, on_gemm=None, on_quant=None, on_block=None):
@@ -389,7 +394,7 @@ class Workload:
         # keep the GPU busy for LEAD_MS while the host enqueues the region
         est = e0.elapsed_time(e1) / max(n, 1)
         self.lead_steps = max(1, min(LEAD_MAX_STEPS,
-                                     math.ceil(LEAD_MS / max(est, 1e-3))))
+                                     math.ceil(self.lead_ms / max(est, 1e-3))))
 
     def graph_lead_in(self, g):
         """Replays of graph ``g`` queued right before its timed replays
@@ -402,7 +407,7 @@ class Workload:
         e1.record()
         torch.cuda.synchronize()
         n = max(1, min(LEAD_MAX_REPLAYS, math.ceil(
-            LEAD_MS / max(e0.elapsed_time(e1), 1e-3))))
+            self.lead_ms / max(e0.elapsed_time(e1), 1e-3))))
         for _ in range(n):
             g.replay()
 
@@ -696,7 +701,7 @@ def run(args, sampler):
         orc = oracle.default()
     wl = D.WORKLOADS[args.config]
     w = Workload(wl, dev, args.qkv, 0 if args.no_check else args.check_rows,
-                 orc, threads, args.graph, args.lead)
+                 orc, threads, args.graph, args.lead, args.lead_ms)
     m = measure(w, args.steps, args.warmup, sampler)
     log(f"[bench] step {m['ms_step']:.3f} ms -> {m['tops']:.1f} TOPS "
         f"({100 * m['tops'] / INT8_PEAK_TOPS:.1f}% of INT8 peak); GEMM calls "
@@ -813,7 +818,8 @@ def run(args, sampler):
 def per_config_entry(wl, dev, orc, threads, args):
     """A compact entry for another workload: value, step statistics, the
     GEMM call's roofline, per-phase rates and its own oracle check."""
-    w = Workload(wl, dev, "auto", 8, orc, threads, "auto", args.lead)
+    w = Workload(wl, dev, "auto", 8, orc, threads, "auto", args.lead,
+                 args.lead_ms)
     m = measure(w, args.per_config_steps, 2)
     check = w.check()
     r = roofline_entry(w.blocks[0], w.M, m["gemm_tops"], m["avg_launch_us"],
