@@ -601,7 +601,16 @@ hipError_t launch_row_op(const uint16_t *x, void *out, float *scale,
       return hipGetLastError();
     }
   }
-  if (chunks <= 11 * 64) {
+  // One wave per row, or a row split over the 4 waves of a work group
+  // (their maxima meet in LDS).  Plain quantization splits rows of more
+  // than 2 chunks per lane: more waves share a row's loads, which pays at
+  // every token count (K = 5376: M = 64 4.2 against 10.0 us, M = 4096 15.4
+  // against 19.1 us, M = 19077 52.7 against 56.3 us).  The renormalizing
+  // kernels, which also write the BF16 row, measured no faster split and
+  // keep one wave per row up to 11 chunks per lane.
+  const bool split = (OP == OP_QUANT || OP == OP_QUANT_W) ? chunks > 2 * 64
+                                                          : chunks > 11 * 64;
+  if (!split) {
     const int ch = (chunks + 63) / 64;
     return launch_rows<1, OP>(x, out, scale, M, (int)K, ch, stream, aux);
   }
