@@ -74,3 +74,31 @@ def test_noalloc_rejects_like_gemm():
                                sw.data_ptr(), bias.data_ptr(), out.data_ptr(),
                                B.OUT_BF16, 64, 200, 256, None)
     assert rc == 2  # W8A8_ERR_SHAPE
+
+
+def test_noalloc_replays_in_a_captured_graph():
+    """The callers this entry point is for include code under HIP graph
+    capture: a captured split-tail call (its partial sums in the scratch),
+    replayed three times with eager calls between the replays that write
+    the same scratch for another shape, matches the eager w8a8_gemm on
+    every replay."""
+    M, N, K = SHAPES[0]
+    args = inputs(M, N, K, 77)
+    want = B.gemm(*args)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    B.gemm_noalloc(*args, out=out)  # one-time set-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.gemm_noalloc(*args, out=out)
+    Mo, No, Ko = SHAPES[1]
+    other = inputs(Mo, No, Ko, 78)
+    other_out = torch.empty((Mo, No), dtype=torch.bfloat16, device="cuda")
+    for r in range(3):
+        print(f"graph replay {r}", flush=True)
+        out.zero_()
+        B.gemm_noalloc(*other, out=other_out)  # dirties the scratch
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16)), r
