@@ -93,8 +93,10 @@ QUANT_SHAPES = [(1, 8), (3, 128), (65, 5376), (64, 5632), (5, 5640),
                 (7, 21504), (2, 90112), (257, 384), (33, 1000),
                 (5000, 5376), (4500, 1000), (6, 90120), (7, 130944),
                 (300, 98304),
-                # one wave per row up to 1024 elements, four waves above
-                (9, 1024), (9, 1032)]
+                # one wave per row up to 1024 elements, four waves above,
+                # two waves from 8192 rows on
+                (9, 1024), (9, 1032), (8192, 1032), (8200, 5376),
+                (8193, 11264)]
 
 
 @pytest.mark.parametrize("M,K", QUANT_SHAPES)
@@ -207,7 +209,7 @@ def test_pow2_renorm_quantize(orc, M, K, in_place):
 
 @pytest.mark.parametrize("N,K", [(5376, 5376), (300, 21504), (7, 8),
                                  (9, 130944), (33, 1000),
-                                 (1000, 14336)])
+                                 (1000, 14336), (8200, 5376)])
 def test_quantize_weight(orc, N, K):
     say(f"quantize_weight N={N} K={K}")
     w = D.activations(N, K, seed=200 + N)

@@ -601,7 +601,7 @@ hipError_t launch_row_op(const uint16_t *x, void *out, float *scale,
       return hipGetLastError();
     }
   }
-  // One wave per row, or a row split over the 4 waves of a work group
+  // One wave per row, or a row split over 2 or 4 waves of a work group
   // (their maxima meet in LDS).  Plain quantization splits rows of more
   // than 2 chunks per lane: more waves share a row's loads, which pays at
   // every token count (K = 5376: M = 64 4.2 against 10.0 us, M = 4096 15.4
@@ -613,6 +613,15 @@ hipError_t launch_row_op(const uint16_t *x, void *out, float *scale,
   if (!split) {
     const int ch = (chunks + 63) / 64;
     return launch_rows<1, OP>(x, out, scale, M, (int)K, ch, stream, aux);
+  }
+  // Many rows: two waves per row, two rows per work group, while a row
+  // fits 44 chunks per lane (K = 5376: M = 19077 51.1 against 52.9 us,
+  // M = 37503 93.5 against 99.2 us; at M = 4096 and below four waves per
+  // row stay faster).
+  if constexpr (OP == OP_QUANT || OP == OP_QUANT_W) {
+    const int ch2 = (chunks + 2 * 64 - 1) / (2 * 64);
+    if (M >= 8192 && ch2 <= 44)
+      return launch_rows<2, OP>(x, out, scale, M, (int)K, ch2, stream, aux);
   }
   const int ch = (chunks + 4 * 64 - 1) / (4 * 64);
   return launch_rows<4, OP>(x, out, scale, M, (int)K, ch, stream, aux);
