@@ -8,6 +8,9 @@ with Q, K and V fused into one GEMM where the benchmark fuses them).
   one token row from every 256-token tile (the large GEMM tiles), at an
   offset that changes from tile to tile, plus the first and last rows;
   each row is compared over every output channel of every projection.
+* w8a8_linear at the three DiT GEMM shapes and 19077 tokens: a row from
+  every 256-token tile against the oracle; the allocation-free GEMM equal
+  to w8a8_gemm (and to linear) on every element.
 * The 50-block chains at 19077 tokens, stage by stage: before every block
   the test reads some rows of the block input the device holds; the oracle
   takes those rows through the block, and the device's codes, scales and
@@ -123,6 +126,36 @@ def test_block_row_per_token_tile(orc, config, fused):
     ref = block_rows(orc, x[rows], params, wl.mlp, wl.o_input)
     compare_block(runner, out, ref, torch.from_numpy(rows).cuda(), wl.name,
                   wl.o_input)
+
+
+# ---------------------------------------------------------------------------
+# w8a8_linear and the allocation-free GEMM at the DiT shapes, 19077 tokens
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K", [(5376, 5376), (21504, 5376), (5376, 21504)])
+def test_linear_and_noalloc_full_size(orc, N, K):
+    M = 19077
+    say(f"w8a8_linear M={M} N={N} K={K}: a row from every 256-token tile; "
+        "w8a8_gemm_noalloc against w8a8_gemm on every element")
+    x = D.activations(M, K, seed=11)
+    w, sw, b = D.weights(N, K, seed=11), D.weight_scales(N, seed=11), \
+        D.bias(N, seed=11)
+    xd, bd = BL.to_device_bf16(x), BL.to_device_bf16(b)
+    wd, swd = torch.from_numpy(w).cuda(), torch.from_numpy(sw).cuda()
+    y = B.linear(xd, wd, swd, bd)
+    torch.cuda.synchronize()
+    rows = tile_rows(M, 256, salt=N % 7)
+    want = orc.linear(x[rows], w, sw, b)
+    got = host_bf16(y[torch.from_numpy(rows).cuda()])
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"linear: {len(bad)} differ, first {bad[:4].tolist()}"
+    q, s = B.quantize_act(xd)
+    ref = B.gemm(q, s, wd, swd, bd)
+    out = torch.empty_like(ref)
+    B.gemm_noalloc(q, s, wd, swd, bd, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(ref.view(torch.int16), y.view(torch.int16))
 
 
 # ---------------------------------------------------------------------------
