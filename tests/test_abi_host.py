@@ -302,9 +302,10 @@ def test_library_shares_torchs_hip_runtime():
     r = subprocess.run([sys.executable, "-c", code], capture_output=True,
                        text=True, timeout=300)
     assert r.returncode == 0, r.stderr
+    import ast
     for line in r.stdout.splitlines():
         key, paths = line.split(" ", 1)
-        assert len(eval(paths)) == 1, line  # one runtime of each kind
+        assert len(ast.literal_eval(paths)) == 1, line  # one of each kind
 
 
 def test_binding_checks_tensors_before_calling():
